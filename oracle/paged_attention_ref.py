@@ -1,0 +1,257 @@
+"""CPU oracle for paged decode attention and the paged KV slot write.
+
+TEST INFRASTRUCTURE ONLY.  This module is the independent definition that the
+GPU library is checked against.  Only the test suite, the smoke check in
+``__graft_entry__`` and the CPU-baseline leg of ``bench.py`` may import it.  The
+library never imports it, and it imports nothing from the library: the two
+share no code.  Its inputs are plain NumPy arrays.
+
+Everything is computed in float64 and written straight from the definitions on
+the pages:
+
+* "vLLM Framework and Inference Engine Design" (vineetganti.com), section
+  "What is the essence of vLLM's PagedAttention?": token ``t`` sits in logical
+  block ``j = floor(t / B)`` at offset ``r = t mod B``; the sequence's block
+  table maps ``j`` to a physical block ``p``; its key and value are
+  ``K_cache[p][r]`` and ``V_cache[p][r]`` in a pool kept per layer; ``T``
+  tokens take ``ceil(T / B)`` blocks.  The page's PyTorch sketch then computes
+  ``softmax(q . K^T / sqrt(d)) . V`` over the first ``T`` gathered tokens.
+* Same page, section "How is vLLM's KV cache paged?": a new token's K and V
+  are copied into slot ``block_table[floor(t / B)] * B + (t mod B)``; the list
+  of these per-token slots is the slot mapping.
+
+Readings taken where the pages leave a step open:
+
+* Pool layout ``[num_blocks][num_kv_heads][block_size][head_dim]``.  The pages
+  leave the layout to the attention backend; the oracle indexes named axes, so
+  the layout is only a convention for its inputs.
+* Grouped-query attention: query head ``h`` reads kv head ``floor(h / G)``
+  with ``G = Hq / Hkv`` (the sudo.vn page, section "How big the KV cache is",
+  only says there are fewer KV heads than query heads).
+* ``scale`` is an argument (the sketch hard-codes ``1/sqrt(head_dim)``); it is
+  the float32 value the GPU receives, widened to float64.
+* ``T = 0`` gives an all-zero output (the sketch's softmax and sum over an
+  empty set).
+* The softmax subtracts the row maximum first, an exact identity.
+* A negative slot in the slot mapping means "no token"; slots must be
+  distinct.
+
+Parity pins (tests/test_oracle_pins.py): contiguous brute force, a torch
+float64 rendering of the page's sketch, placement invariance, shared-prefix
+equality, closed forms (T = 1, q = 0, equal keys, hard maximum) and the pages'
+printed byte and block arithmetic.  No function here is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+# dtype tags shared by the inputs: 'f32' and 'f16' are NumPy float arrays;
+# 'bf16' arrays hold the raw 16-bit patterns as uint16 (NumPy has no bfloat16).
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+
+
+# ---------------------------------------------------------------------------
+# element decoding
+# ---------------------------------------------------------------------------
+def to_float64(arr: np.ndarray, dtype: str) -> np.ndarray:
+    """Exact float64 value of every element.
+
+    A bfloat16 number is the upper half of a float32, so its bit pattern
+    shifted left by 16 is that float32; fp16 and fp32 widen exactly.
+    """
+    if dtype == "bf16":
+        if arr.dtype != np.uint16:
+            raise TypeError("bf16 arrays are carried as uint16 bit patterns")
+        wide = arr.astype(np.uint32) << np.uint32(16)
+        return wide.view(np.float32).astype(np.float64)
+    if dtype == "f16":
+        if arr.dtype != np.float16:
+            raise TypeError("f16 arrays must be numpy.float16")
+        return arr.astype(np.float64)
+    if dtype == "f32":
+        if arr.dtype != np.float32:
+            raise TypeError("f32 arrays must be numpy.float32")
+        return arr.astype(np.float64)
+    raise ValueError(f"unknown dtype tag {dtype!r}")
+
+
+# ---------------------------------------------------------------------------
+# block arithmetic ("What is the essence of vLLM's PagedAttention?")
+# ---------------------------------------------------------------------------
+def blocks_for_tokens(num_tokens: int, block_size: int) -> int:
+    """ceil(T / B): the number of blocks a sequence of T tokens holds."""
+    return -(-int(num_tokens) // int(block_size))
+
+
+def token_location(table_row, t, block_size: int):
+    """Physical block and in-block offset of token t of one sequence.
+
+    Logical block j = floor(t / B), offset r = t mod B, physical block
+    p = block_table[j].  ``t`` may be an int or an integer array.
+    """
+    j = t // block_size
+    r = t % block_size
+    return np.asarray(table_row)[j], r
+
+
+def slot_of_token(table_row, t: int, block_size: int) -> int:
+    """The slot-mapping entry of token t: block_table[floor(t/B)] * B + (t mod B)
+    ("How is vLLM's KV cache paged?", the writing step)."""
+    p, r = token_location(table_row, t, block_size)
+    return int(p) * block_size + int(r)
+
+
+def slot_location(slot: int, block_size: int) -> tuple[int, int]:
+    """Inverse of the slot formula: (physical block, offset) of a slot."""
+    return slot // block_size, slot % block_size
+
+
+def kv_head_for_query_head(h: int, num_q_heads: int, num_kv_heads: int) -> int:
+    """Grouped-query attention: contiguous groups of G = Hq / Hkv query heads
+    share one kv head (a reading; the pages only state Hkv < Hq)."""
+    group = num_q_heads // num_kv_heads
+    return h // group
+
+
+# ---------------------------------------------------------------------------
+# the slot write (reshape_and_cache)
+# ---------------------------------------------------------------------------
+def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k: np.ndarray,
+             v: np.ndarray, slot_mapping: np.ndarray, block_size: int):
+    """Copy each new token's K and V into its slot; return the new pools.
+
+    k_pool, v_pool: [num_blocks][Hkv][B][D]; k, v: [num_tokens][Hkv][D] of the
+    same element type; slot_mapping: int [num_tokens].  A negative slot skips
+    its token.  The copy is of raw elements, so the result is bit-exact.
+    """
+    num_blocks, num_kv_heads, bs, head_dim = k_pool.shape
+    if bs != block_size:
+        raise ValueError("pool block size does not match block_size")
+    if k.shape != (len(slot_mapping), num_kv_heads, head_dim) or v.shape != k.shape:
+        raise ValueError("k/v must be [num_tokens][Hkv][D]")
+    live = [int(s) for s in slot_mapping if int(s) >= 0]
+    if len(set(live)) != len(live):
+        raise ValueError("slot mapping repeats a slot")
+    if any(s >= num_blocks * block_size for s in live):
+        raise ValueError("slot outside the pool")
+    k_new = k_pool.copy()
+    v_new = v_pool.copy()
+    for n, s in enumerate(slot_mapping):
+        s = int(s)
+        if s < 0:
+            continue
+        p, r = slot_location(s, block_size)
+        k_new[p, :, r, :] = k[n]
+        v_new[p, :, r, :] = v[n]
+    return k_new, v_new
+
+
+# ---------------------------------------------------------------------------
+# decode attention through the block table
+# ---------------------------------------------------------------------------
+def gather_tokens(pool: np.ndarray, table_row, num_tokens: int,
+                  block_size: int, dtype: str) -> np.ndarray:
+    """float64 [T][Hkv][D]: the T cached rows of one sequence, in token order,
+    each read at (p, r) = token_location(t) for t = 0 .. T-1."""
+    num_blocks = pool.shape[0]
+    n_blocks = blocks_for_tokens(num_tokens, block_size)
+    if n_blocks > len(table_row):
+        raise ValueError("context longer than the block table")
+    t = np.arange(num_tokens, dtype=np.int64)
+    p, r = token_location(table_row, t, block_size)
+    if num_tokens and (p.min() < 0 or p.max() >= num_blocks):
+        raise ValueError("block table entry outside the pool")
+    # advanced indices on axes 0 and 2 -> shape [T][Hkv][D]
+    return to_float64(pool[p, :, r, :], dtype)
+
+
+def attend(q_h: np.ndarray, keys: np.ndarray, values: np.ndarray,
+           scale: float) -> np.ndarray:
+    """softmax(scale * keys . q_h) . values for one query row, in float64.
+
+    q_h: [D]; keys, values: [T][D].  The maximum score is subtracted before the
+    exponential (an identity that keeps exp finite)."""
+    scores = scale * (keys @ q_h)
+    weights = np.exp(scores - scores.max())
+    return (weights @ values) / weights.sum()
+
+
+def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+           block_tables: np.ndarray, context_lens, scale: float,
+           dtype: str, seqs=None) -> np.ndarray:
+    """Decode-step attention for every (sequence, query head); float64 out.
+
+    q: [N][Hq][D]; pools: [num_blocks][Hkv][B][D]; block_tables: int [N][MB];
+    context_lens: int [N] (T_i counts the newest token, whose K/V is already in
+    the pool).  ``seqs`` restricts the work to some sequences (their rows of the
+    result are filled, the others are left NaN) for sampled checks at full size.
+    """
+    num_seqs, num_q_heads, head_dim = q.shape
+    _, num_kv_heads, block_size, pool_dim = k_pool.shape
+    if pool_dim != head_dim or v_pool.shape != k_pool.shape:
+        raise ValueError("q, k_pool and v_pool disagree on shapes")
+    if num_q_heads % num_kv_heads:
+        raise ValueError("query heads must be a multiple of kv heads")
+    sc = float(np.float32(scale))
+    out = np.full((num_seqs, num_q_heads, head_dim), np.nan, dtype=np.float64)
+    q64 = to_float64(q, dtype)
+    todo = range(num_seqs) if seqs is None else seqs
+    for i in todo:
+        T = int(context_lens[i])
+        if T == 0:
+            out[i] = 0.0
+            continue
+        keys = gather_tokens(k_pool, block_tables[i], T, block_size, dtype)
+        values = gather_tokens(v_pool, block_tables[i], T, block_size, dtype)
+        for h in range(num_q_heads):
+            g = kv_head_for_query_head(h, num_q_heads, num_kv_heads)
+            out[i, h] = attend(q64[i, h], keys[:, g, :], values[:, g, :], sc)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# byte and block accounting
+# ---------------------------------------------------------------------------
+def kv_bytes_per_token(layers: int, kv_heads: int, head_dim: int,
+                       dtype_bytes: int) -> int:
+    """2 (key and value) x layers x kv heads x head_dim x bytes per element
+    (sudo.vn page, "How big the KV cache is: a formula and a real
+    measurement")."""
+    return 2 * layers * kv_heads * head_dim * dtype_bytes
+
+
+def block_bytes(layers: int, block_size: int, kv_heads: int, head_dim: int,
+                dtype_bytes: int) -> int:
+    """Bytes of one block across all layers, K and V
+    ("How is vLLM's KV cache paged?", pool set-up)."""
+    return 2 * layers * block_size * kv_heads * head_dim * dtype_bytes
+
+
+def kv_bytes_read(context_lens, kv_heads: int, head_dim: int,
+                  dtype_bytes: int) -> int:
+    """KV bytes one decode step must read for one layer: every cached token's
+    K and V once per kv head (the step-time model in "How does vLLM's
+    scheduling achieve both minimal latency and maximum throughput?" charges
+    every cached token)."""
+    total_tokens = int(np.sum(np.asarray(context_lens, dtype=np.int64)))
+    return 2 * kv_heads * head_dim * dtype_bytes * total_tokens
+
+
+def wasted_slots_paged(context_lens, block_size: int) -> int:
+    """Allocated but unused slots with paging: sum of ceil(T/B)*B - T
+    ("What operations can cause memory fragmentation ...")."""
+    return sum(blocks_for_tokens(T, block_size) * block_size - int(T)
+               for T in context_lens)
+
+
+def wasted_slots_contiguous(context_lens, max_len: int) -> int:
+    """Reserved but unused slots when every request reserves max_len."""
+    return sum(int(max_len) - int(T) for T in context_lens)
+
+
+def static_batch_useful_fraction(prompts, outputs) -> float:
+    """sum(p_i + o_i) / (n * (max p + max o)) ("Why is batching multiple
+    requests difficult for traditional inference engines?")."""
+    n = len(prompts)
+    return (sum(prompts) + sum(outputs)) / (n * (max(prompts) + max(outputs)))
