@@ -1,0 +1,207 @@
+"""Paged decode-attention benchmark on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
+
+One step is the whole hot path for one decode batch: pa_write_kv of the
+batch's new tokens, then pa_decode (the partitioned attention kernel and,
+when a sequence spans several partitions, the log-sum-exp merge).  Inputs are
+resident in HBM before timing starts.  To keep the timed reads cold in the
+GPU caches, steps rotate over several copies of the pools (together well above
+the 256 MB Infinity Cache).
+
+Printed: one JSON line with the metric (KV bytes read per second, TB/s), the
+roofline of the decode call measured with HIP events on its stream, and the
+CPU oracle timed on a bounded sample as a baseline.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+
+WORKLOAD_NAMES = {
+    1: "tiny-decode-f32: 4 seqs, 4q/4kv heads, d64, B4, lens [7,8,9,8]",
+    2: "qwen2-0.5b-decode-f16: 32 seqs, 14q/2kv heads, d64, B16, lens U{1..4096}",
+    3: "llama3-8b-decode-bf16: 256 seqs, 32q/8kv heads, d128, B16, lognormal lens mean~400 cap 4096, 256 new tokens written",
+    4: "llama2-7b-decode-f16: 64 seqs, 32q/32kv heads, d128, B16, every len 4096",
+    5: "prefix-shared-decode-bf16: 12 seqs, 64q/8kv heads, d128, B16, 1800-token shared prefix + U{0..512} + 1",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--seed", type=int, default=None)
+    ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
+    ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle as it stands (write, then decode), on the same host arrays,
+    one BLAS thread; repeated over growing sequence samples until the budget
+    is spent.  Returns TB/s of KV bytes read, the sample description, cores."""
+    import numpy as np
+
+    import oracle.paged_attention_ref as ref
+    from threadpoolctl import threadpool_limits
+    bytes_done, secs, reps = 0, 0.0, 0
+    n = w.num_seqs
+    with threadpool_limits(1):
+        while secs < budget_s and reps < 100:
+            t0 = time.perf_counter()
+            k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size)
+            ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
+                       seqs=np.arange(n))
+            secs += time.perf_counter() - t0
+            bytes_done += kv_bytes_per_step(w)
+            reps += 1
+    sample = f"{reps} full steps of the same batch (write + decode, all {n} seqs), {secs:.1f} s"
+    return bytes_done / secs / 1e12, sample, 1
+
+
+def kv_bytes_per_step(w) -> int:
+    """Algorithmic KV bytes of one decode step: every cached token's K and V
+    row, once per kv head."""
+    return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(w.context_lens.astype("int64").sum())
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": args.gpus}), flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import workloads
+    from paged_kv_cache_75_amd import (pa_decode, pa_decode_workspace_bytes, pa_write_kv,
+                                       pool_desc)
+
+    if not torch.cuda.is_available():
+        sys.exit("bench.py needs a GPU")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    cfg = args.config
+    seed = cfg if args.seed is None else args.seed
+    w = workloads.make(cfg, seed=seed, poison=False)
+
+    def up(a, dt):
+        a = np.ascontiguousarray(a)
+        if dt == "bf16":
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(a).to(dev)
+
+    q = up(w.q, w.dtype)
+    bt = up(w.block_tables.astype(np.int32), None)
+    cl = up(w.context_lens.astype(np.int32), None)
+    slots = up(w.slot_mapping.astype(np.int32), None)
+    nk, nv = up(w.new_k, w.dtype), up(w.new_v, w.dtype)
+    k0, v0 = up(w.k_pool, w.dtype), up(w.v_pool, w.dtype)
+    pool_bytes = 2 * k0.numel() * k0.element_size()
+    reps = args.replicas or max(1, min(8, -(-(1 << 30) // pool_bytes) + 1))
+    pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
+    out = torch.empty_like(q)
+    desc = pool_desc(k0)
+    ws_bytes = pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, desc, w.max_context_len,
+                                         args.partition)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    writes = cfg in (3, 5)
+
+    def step(k):
+        kp, vp = pools[k % reps]
+        if writes:
+            pa_write_kv(nk, nv, slots, kp, vp)
+        pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
+                  workspace=ws, partition_tokens=args.partition)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(K)]
+    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        kp, vp = pools[k % reps]
+        if writes:
+            pa_write_kv(nk, nv, slots, kp, vp)
+        ev[k][0].record(stream)
+        pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
+                  workspace=ws, partition_tokens=args.partition)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    kv_bytes = kv_bytes_per_step(w)
+    ms_per_step = (t1 - t0) * 1e3 / K
+    decode_ms = [a.elapsed_time(b) for a, b in ev]
+    decode_ms_mean = sum(decode_ms) / len(decode_ms)
+    achieved = kv_bytes / (decode_ms_mean * 1e-3) / 1e9
+    value = kv_bytes / (ms_per_step * 1e-3) / 1e12
+
+    result = {
+        "metric": "paged decode attention: KV bytes read/s (TB/s), % HBM peak, us/step",
+        "value": round(value, 4),
+        "unit": "TB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "pct_hbm_peak": round(100 * value * 1e3 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": WORKLOAD_NAMES[cfg],
+            "seed": seed,
+            "num_seqs": w.num_seqs,
+            "sum_context_tokens": int(w.context_lens.sum()),
+            "max_context_len": w.max_context_len,
+            "kv_bytes_per_step": kv_bytes,
+            "new_tokens_written": int((w.slot_mapping >= 0).sum()) if writes else 0,
+            "pool_copies_rotated": reps,
+            "partition_tokens": args.partition or "auto",
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "pa_decode (partition kernel + log-sum-exp merge)",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None,
+            "decode_us_mean": round(decode_ms_mean * 1e3, 2),
+            "decode_us_min": round(min(decode_ms) * 1e3, 2),
+        },
+    }
+    if not args.no_cpu_baseline:
+        v, sample, cores = cpu_baseline(w, args.cpu_seconds)
+        result["cpu_baseline"] = {"value": round(v, 6), "unit": "TB/s", "cores": cores,
+                                  "kind": "oracle", "sample": sample}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * paged_attention.h -- C ABI of the MI355X (gfx950) paged decode-attention
+ * library (libpa.so).
+ *
+ * The library implements the two kernels on the hot path of PagedAttention:
+ *
+ *   pa_write_kv  copies each new token's key and value rows into its slot of a
+ *                per-layer block pool (the slot write of "vLLM Framework and
+ *                Inference Engine Design", section "How is vLLM's KV cache
+ *                paged?": slot = block_table[floor(t/B)] * B + (t mod B)).
+ *   pa_decode    computes, for every sequence i and query head h,
+ *                  out[i][h] = softmax(scale * q[i][h] . K_i^T) . V_i
+ *                over the T_i cached tokens of sequence i, reading token t
+ *                from physical block block_tables[i][floor(t/B)] at offset
+ *                t mod B (same page, section "What is the essence of vLLM's
+ *                PagedAttention?").
+ *
+ * Conventions shared by every entry point:
+ *
+ *   - Every buffer argument is a DEVICE pointer owned by the caller.  The
+ *     library never allocates, frees or keeps a reference to caller memory.
+ *   - Work is enqueued on `stream` (a hipStream_t passed as void*; NULL is the
+ *     null stream) and the call returns without synchronizing.  Results are
+ *     valid once the stream reaches that point.  A decode that must see a
+ *     token written by pa_write_kv has to be enqueued after that write on the
+ *     same stream (or be ordered after it by the caller).
+ *   - Arguments are validated on the host from the scalar arguments only; on
+ *     any error the call returns a status and enqueues nothing.  Device
+ *     arrays (slot_mapping, block_tables, context_lens) are never read on the
+ *     host; their contract is stated per entry point.  Breaking it gives
+ *     unspecified output values but no access outside the buffers: the
+ *     kernels skip slots outside the pool, clamp context lengths into
+ *     [0, max_context_len] and clamp block-table entries into the pool.
+ *   - Element types: the pool, the new k/v rows, q and out share one element
+ *     type (pa_dtype).  Accumulation is in float32.
+ *   - Pool layout (both pools): dense [num_blocks][num_kv_heads][block_size]
+ *     [head_dim], row-major.  One (block, kv head) pair is one contiguous run
+ *     of block_size * head_dim elements.
+ *   - Integer arrays are int32.
+ */
+#ifndef PAGED_ATTENTION_H
+#define PAGED_ATTENTION_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pa_status {
+  PA_OK = 0,
+  PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid shape this build does not handle   */
+  PA_ERR_WORKSPACE_TOO_SMALL = 3,
+  PA_ERR_HIP = 4                 /* a HIP runtime call or a launch failed      */
+} pa_status;
+
+typedef enum pa_dtype {
+  PA_F32 = 0,
+  PA_F16 = 1,
+  PA_BF16 = 2
+} pa_dtype;
+
+/* One layer's block pool.  block_size must be a power of two in [1, 256];
+ * head_dim is 64 or 128; num_blocks * block_size must stay below 2^31. */
+typedef struct pa_pool_desc {
+  int32_t num_blocks;
+  int32_t block_size;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t dtype;                 /* a pa_dtype value */
+} pa_pool_desc;
+
+/*
+ * pa_write_kv -- place new tokens' K and V rows into their pool slots.
+ *
+ *   k, v          [num_tokens][num_kv_heads][head_dim], pool element type.
+ *   slot_mapping  int32 [num_tokens]; slot s >= 0 sends token n to physical
+ *                 block s / block_size at offset s % block_size, for every kv
+ *                 head.  s < 0 skips the token (padding).  Live slots must be
+ *                 distinct and below num_blocks * block_size.
+ *   k_pool, v_pool  pools described by *pool; only the addressed rows change.
+ *
+ * The copy is of raw element bits, so the pools match a host-side copy bit
+ * for bit.  num_tokens == 0 is a no-op returning PA_OK.
+ */
+pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_pool, void* v_pool,
+                      const pa_pool_desc* pool, void* stream);
+
+/*
+ * pa_decode_workspace_bytes -- size in bytes of the float32 workspace that
+ * pa_decode needs for these sizes (0 when every sequence fits in a single
+ * context partition, in which case workspace may be NULL).  partition_tokens
+ * is the context partition length (a multiple of 16), or 0 for the library's
+ * choice.  Returns 0 also for invalid sizes (pa_decode reports those).
+ */
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 const pa_pool_desc* pool, int32_t max_context_len,
+                                 int32_t partition_tokens);
+
+/*
+ * pa_decode -- one decode step of paged attention for num_seqs sequences.
+ *
+ *   q             [num_seqs][num_q_heads][head_dim].
+ *   k_pool, v_pool, pool   the layer's pools (see above).
+ *   block_tables  int32 [num_seqs][max_blocks_per_seq]; entry j of row i is
+ *                 the physical block of tokens j*B .. j*B+B-1 of sequence i.
+ *                 Only entries j < ceil(T_i / B) are read; each must lie in
+ *                 [0, num_blocks).  Entries past them may hold anything.
+ *   context_lens  int32 [num_seqs]; T_i counts the token being decoded, whose
+ *                 K/V must already be in the pool.  0 <= T_i <= max_context_len.
+ *                 T_i == 0 yields an all-zero output row.
+ *   max_context_len  host-side upper bound on every T_i; sizes the launch.
+ *                 Must be <= max_blocks_per_seq * block_size.
+ *   num_q_heads   a multiple of num_kv_heads.  Query head h reads kv head
+ *                 h / (num_q_heads / num_kv_heads) (contiguous groups).
+ *   scale         multiplies q . k before the softmax (1/sqrt(head_dim) for
+ *                 standard attention).
+ *   out           [num_seqs][num_q_heads][head_dim], rounded to nearest even.
+ *   workspace     float32 scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes for the same sizes and partition_tokens; its contents
+ *                 on entry do not matter.  Calls sharing one workspace must be
+ *                 ordered on one stream.
+ *   partition_tokens  context partition length (multiple of 16), or 0 for
+ *                 the library's choice.  Sequences longer than one partition
+ *                 are split, and the per-partition results are merged by a
+ *                 log-sum-exp reduction; the result does not depend on the
+ *                 partition length beyond float32 rounding.
+ *
+ * Supported: head_dim 64 or 128; query heads per kv head 1..8 or 16.
+ */
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t partition_tokens, void* stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char* pa_status_string(pa_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGED_ATTENTION_H */

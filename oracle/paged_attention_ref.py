@@ -118,12 +118,15 @@ def kv_head_for_query_head(h: int, num_q_heads: int, num_kv_heads: int) -> int:
 # the slot write (reshape_and_cache)
 # ---------------------------------------------------------------------------
 def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k: np.ndarray,
-             v: np.ndarray, slot_mapping: np.ndarray, block_size: int):
+             v: np.ndarray, slot_mapping: np.ndarray, block_size: int,
+             inplace: bool = False):
     """Copy each new token's K and V into its slot; return the new pools.
 
     k_pool, v_pool: [num_blocks][Hkv][B][D]; k, v: [num_tokens][Hkv][D] of the
     same element type; slot_mapping: int [num_tokens].  A negative slot skips
     its token.  The copy is of raw elements, so the result is bit-exact.
+    With ``inplace`` the given pools are updated and returned (no copy of a
+    multi-GiB pool).
     """
     num_blocks, num_kv_heads, bs, head_dim = k_pool.shape
     if bs != block_size:
@@ -135,8 +138,8 @@ def write_kv(k_pool: np.ndarray, v_pool: np.ndarray, k: np.ndarray,
         raise ValueError("slot mapping repeats a slot")
     if any(s >= num_blocks * block_size for s in live):
         raise ValueError("slot outside the pool")
-    k_new = k_pool.copy()
-    v_new = v_pool.copy()
+    k_new = k_pool if inplace else k_pool.copy()
+    v_new = v_pool if inplace else v_pool.copy()
     for n, s in enumerate(slot_mapping):
         s = int(s)
         if s < 0:

@@ -1,0 +1,191 @@
+"""Thin ctypes binding of libpa.so, with the C entry points' names.
+
+Only argument marshalling happens here: shapes and dtypes of the torch tensors
+are checked and turned into pointers and sizes, then the C function is called
+on the current torch stream.  Every step of the computation runs in the HIP
+kernels.  If the library has not been built, the first call raises
+RuntimeError; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libpa.so")
+HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "include", "paged_attention.h")
+
+PA_OK = 0
+PA_ERR_INVALID_ARGUMENT = 1
+PA_ERR_UNSUPPORTED = 2
+PA_ERR_WORKSPACE_TOO_SMALL = 3
+PA_ERR_HIP = 4
+
+PA_F32, PA_F16, PA_BF16 = 0, 1, 2
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {pa_status_string(status)} ({status})")
+        self.status = status
+
+
+class pa_pool_desc(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def declared_functions(header: str = HEADER_PATH) -> list[str]:
+    """Names of the functions include/paged_attention.h declares."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def lib():
+    """The loaded library (raises RuntimeError when it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"libpa.so is not built ({LIB_PATH}); run __graft_entry__.build()")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    desc = ctypes.POINTER(pa_pool_desc)
+    L.pa_write_kv.argtypes = [vp, vp, vp, i32, vp, vp, desc, vp]
+    L.pa_write_kv.restype = ctypes.c_int
+    L.pa_decode_workspace_bytes.argtypes = [i32, i32, desc, i32, i32]
+    L.pa_decode_workspace_bytes.restype = sz
+    L.pa_decode.argtypes = [vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                            vp, vp, sz, i32, vp]
+    L.pa_decode.restype = ctypes.c_int
+    L.pa_status_string.argtypes = [ctypes.c_int]
+    L.pa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def pa_status_string(status: int) -> str:
+    return lib().pa_status_string(int(status)).decode()
+
+
+# ---------------------------------------------------------------------------
+# torch-facing marshalling
+# ---------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def dtype_code(t) -> int:
+    torch = _torch()
+    codes = {torch.float32: PA_F32, torch.float16: PA_F16, torch.bfloat16: PA_BF16}
+    if t.dtype not in codes:
+        raise ValueError(f"unsupported element type {t.dtype}")
+    return codes[t.dtype]
+
+
+def pool_desc(k_pool) -> pa_pool_desc:
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    nb, hkv, bs, d = (int(x) for x in k_pool.shape)
+    return pa_pool_desc(nb, bs, hkv, d, dtype_code(k_pool))
+
+
+def _stream(stream):
+    if stream is not None:
+        return int(stream) if not hasattr(stream, "cuda_stream") else int(stream.cuda_stream)
+    return int(_torch().cuda.current_stream().cuda_stream)
+
+
+def _check(t, name, dtype=None, dim=None, device=None):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dimensions")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def pa_write_kv(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Copy k[n], v[n] ([num_tokens][Hkv][D]) into slot slot_mapping[n] of the
+    pools; negative slots are skipped."""
+    torch = _torch()
+    desc = pool_desc(k_pool)
+    dev = k_pool.device
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k, "k"), (v, "v")):
+        _check(t, n, dtype=k_pool.dtype, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(slot_mapping, "slot_mapping", dtype=torch.int32, dim=1, device=dev)
+    n_tok = int(slot_mapping.shape[0])
+    want = (n_tok, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k and v must be {want}")
+    st = lib().pa_write_kv(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), n_tok,
+                           k_pool.data_ptr(), v_pool.data_ptr(), ctypes.byref(desc),
+                           _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_write_kv")
+
+
+def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, desc: pa_pool_desc,
+                              max_context_len: int, partition_tokens: int = 0) -> int:
+    return int(lib().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads),
+                                               ctypes.byref(desc), int(max_context_len),
+                                               int(partition_tokens)))
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
+              max_context_len=None, workspace=None, partition_tokens: int = 0,
+              stream=None):
+    """Paged decode attention; returns ``out`` ([N][Hq][D], pool dtype).
+
+    ``max_context_len`` is the host bound on context_lens; when omitted it is
+    read from the device (a synchronizing copy).  ``workspace`` is a uint8 or
+    float32 device tensor of at least pa_decode_workspace_bytes(...) bytes;
+    when omitted a fresh one is taken from torch's caching allocator."""
+    torch = _torch()
+    desc = pool_desc(k_pool)
+    dev = k_pool.device
+    _check(k_pool, "k_pool")
+    _check(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(q, "q", dtype=k_pool.dtype, dim=3, device=dev)
+    _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    n, hq, d = (int(x) for x in q.shape)
+    if d != desc.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if n else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, device=dev)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError("out must have q's shape")
+    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, partition_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                         ctypes.byref(desc), block_tables.data_ptr(),
+                         int(block_tables.shape[1]), context_lens.data_ptr(), n,
+                         int(max_context_len), hq, float(scale), out.data_ptr(),
+                         workspace.data_ptr(), ws_bytes, int(partition_tokens),
+                         _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode")
+    return out

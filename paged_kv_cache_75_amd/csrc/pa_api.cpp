@@ -1,0 +1,103 @@
+// C entry points of libpa: validate on the host, plan, launch on the
+// caller's stream.  Nothing here allocates or synchronizes.
+#include <cmath>
+
+#include <hip/hip_runtime_api.h>
+
+#include "paged_attention.h"
+#include "pa_kernels.h"
+#include "pa_plan.h"
+
+extern "C" {
+
+pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, void* k_pool, void* v_pool,
+                      const pa_pool_desc* pool, void* stream) {
+  const pa_status s = pa::check_write(k, v, slot_mapping, num_tokens, k_pool, v_pool, pool);
+  if (s != PA_OK || num_tokens == 0) return s;
+  pa::WriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_tokens = num_tokens;
+  a.num_slots = pool->num_blocks * pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.row_bytes = pool->head_dim * pa::dtype_bytes(pool->dtype);
+  int32_t lb = 0;
+  while ((1 << lb) < pool->block_size) ++lb;
+  a.log2_block = lb;
+  return pa::launch_write_kv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                                : PA_ERR_HIP;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 const pa_pool_desc* pool, int32_t max_context_len,
+                                 int32_t partition_tokens) {
+  pa::DecodePlan plan;
+  if (pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len, -1, partition_tokens,
+                      &plan) != PA_OK)
+    return 0;
+  return plan.ws_bytes;
+}
+
+pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
+                    const pa_pool_desc* pool, const int32_t* block_tables,
+                    int32_t max_blocks_per_seq, const int32_t* context_lens,
+                    int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                    float scale, void* out, void* workspace, size_t workspace_bytes,
+                    int32_t partition_tokens, void* stream) {
+  pa::DecodePlan plan;
+  pa_status s = pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len,
+                                max_blocks_per_seq, partition_tokens, &plan);
+  if (s != PA_OK) return s;
+  if (max_blocks_per_seq <= 0 && num_seqs > 0) return PA_ERR_INVALID_ARGUMENT;
+  s = pa::check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out, num_seqs);
+  if (s != PA_OK) return s;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (plan.ws_bytes > 0) {
+    if (!workspace) return PA_ERR_INVALID_ARGUMENT;
+    if (workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
+    if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARGUMENT;
+  }
+  if (num_seqs == 0) return PA_OK;
+
+  pa::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws_o = static_cast<float*>(workspace);
+  a.ws_ml = plan.ws_bytes
+                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset)
+                : nullptr;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
+  a.log2_block = plan.log2_block;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.partition_tokens = plan.partition_tokens;
+  a.num_partitions = plan.num_partitions;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  const hipError_t e = pa::launch_decode(a, pool->dtype, pool->head_dim, plan.group,
+                                         static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+const char* pa_status_string(pa_status status) {
+  switch (status) {
+    case PA_OK: return "PA_OK";
+    case PA_ERR_INVALID_ARGUMENT: return "PA_ERR_INVALID_ARGUMENT";
+    case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
+    case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
+    case PA_ERR_HIP: return "PA_ERR_HIP";
+    default: return "PA_UNKNOWN_STATUS";
+  }
+}
+
+}  // extern "C"

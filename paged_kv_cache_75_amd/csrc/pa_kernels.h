@@ -1,0 +1,53 @@
+// Internal launch interface between the C entry points and the HIP kernels.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include <hip/hip_runtime_api.h>
+
+#include "pa_plan.h"
+
+namespace pa {
+
+struct WriteArgs {
+  const void* k;
+  const void* v;
+  const int32_t* slot_mapping;
+  void* k_pool;
+  void* v_pool;
+  int32_t num_tokens;
+  int32_t num_slots;        // num_blocks * block_size; larger slots are skipped
+  int32_t num_kv_heads;
+  int32_t row_bytes;        // head_dim * element bytes
+  int32_t log2_block;
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  void* out;
+  float* ws_o;              // [num_seqs][num_q_heads][num_partitions][head_dim]
+  float* ws_ml;             // [num_seqs][num_q_heads][num_partitions][2]: max, sum
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t num_blocks;
+  int32_t log2_block;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;  // lengths above it are clamped to it
+  int32_t partition_tokens;
+  int32_t num_partitions;
+  float scale_log2;         // scale * log2(e): scores live in the exp2 domain
+};
+
+hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+
+// dtype is a pa_dtype value; head_dim 64/128; group as planned.
+hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, int32_t head_dim,
+                         int32_t group, hipStream_t stream);
+
+}  // namespace pa

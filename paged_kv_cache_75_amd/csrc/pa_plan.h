@@ -1,0 +1,46 @@
+// Host-side argument checks and launch planning for libpa.  Plain C++ with no
+// HIP dependency, so it also builds with g++ (and sanitizers) for host tests.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "paged_attention.h"
+
+namespace pa {
+
+// Tokens per compute tile: one 16-column MFMA tile of keys.
+constexpr int32_t kTileTokens = 16;
+// Largest block-table slice one decode workgroup stages in LDS.
+constexpr int32_t kTableSliceCap = 1024;
+// Largest context partition.
+constexpr int32_t kMaxPartitionTokens = 8192;
+
+int32_t dtype_bytes(int32_t dtype);   // 0 for an unknown dtype
+
+pa_status check_pool(const pa_pool_desc* pool);
+
+pa_status check_write(const void* k, const void* v, const int32_t* slot_mapping,
+                      int32_t num_tokens, const void* k_pool, const void* v_pool,
+                      const pa_pool_desc* pool);
+
+struct DecodePlan {
+  int32_t group = 0;              // query heads per kv head
+  int32_t partition_tokens = 0;   // tokens per context partition
+  int32_t num_partitions = 0;     // partitions of the longest sequence
+  int32_t log2_block = 0;
+  size_t ws_bytes = 0;            // 0 when num_partitions == 1
+  size_t ws_ml_offset = 0;        // byte offset of the (max, sum) pairs
+};
+
+// Shape checks plus the launch plan.  max_blocks_per_seq < 0 skips the
+// table-width check (used by the workspace query).
+pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc* pool,
+                      int32_t max_context_len, int32_t max_blocks_per_seq,
+                      int32_t partition_tokens, DecodePlan* plan);
+
+pa_status check_decode_pointers(const void* q, const void* k_pool, const void* v_pool,
+                                const int32_t* block_tables, const int32_t* context_lens,
+                                const void* out, int32_t num_seqs);
+
+}  // namespace pa

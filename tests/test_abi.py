@@ -1,0 +1,103 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header
+declares, and rejects bad arguments with the documented status before any
+HIP call (so no GPU is needed)."""
+import ctypes
+import os
+
+import pytest
+
+from paged_kv_cache_75_amd import binding as B
+
+pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so not built")
+
+
+def test_exports_every_declared_function():
+    names = B.declared_functions()
+    assert {"pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_status_string"} <= set(names)
+    L = ctypes.CDLL(B.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"libpa.so does not export {n}"
+
+
+def test_status_strings():
+    for code, name in ((0, "PA_OK"), (1, "PA_ERR_INVALID_ARGUMENT"), (2, "PA_ERR_UNSUPPORTED"),
+                       (3, "PA_ERR_WORKSPACE_TOO_SMALL"), (4, "PA_ERR_HIP")):
+        assert B.pa_status_string(code) == name
+    assert B.pa_status_string(99) == "PA_UNKNOWN_STATUS"
+
+
+def desc(nb=64, bs=16, hkv=2, d=128, dt=B.PA_BF16):
+    return B.pa_pool_desc(nb, bs, hkv, d, dt)
+
+
+FAKE = 0x1000    # never dereferenced: every call below fails validation first
+
+
+def decode(d, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=8, cl=FAKE, n=4, maxlen=100, hq=8,
+             scale=0.1, out=FAKE, ws=FAKE, wsb=1 << 20, part=0)
+    a.update(kw)
+    return B.lib().pa_decode(a["q"], a["k"], a["v"], ctypes.byref(d) if d is not None else None,
+                             a["bt"], a["mb"], a["cl"], a["n"], a["maxlen"], a["hq"],
+                             a["scale"], a["out"], a["ws"], a["wsb"], a["part"], None)
+
+
+@pytest.mark.parametrize("kw,bad_desc,want", [
+    (dict(hq=7), None, B.PA_ERR_INVALID_ARGUMENT),          # Hq % Hkv != 0
+    (dict(hq=2 * 9), None, B.PA_ERR_UNSUPPORTED),            # group 9
+    (dict(maxlen=8 * 16 + 1), None, B.PA_ERR_INVALID_ARGUMENT),  # > MB * B
+    (dict(maxlen=-1), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(n=-1), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(q=None), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(cl=None), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(out=None), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(part=24), None, B.PA_ERR_INVALID_ARGUMENT),        # not a multiple of 16
+    (dict(part=16384), None, B.PA_ERR_UNSUPPORTED),
+    (dict(scale=float("nan")), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(maxlen=100, part=16, ws=None), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(maxlen=100, part=16, wsb=16), None, B.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(), "dtype", B.PA_ERR_INVALID_ARGUMENT),
+    (dict(), "head_dim", B.PA_ERR_UNSUPPORTED),
+    (dict(), "block_size", B.PA_ERR_UNSUPPORTED),
+    (dict(), "null", B.PA_ERR_INVALID_ARGUMENT),
+    (dict(), "huge_pool", B.PA_ERR_UNSUPPORTED),
+])
+def test_decode_validation(kw, bad_desc, want):
+    d = desc()
+    if bad_desc == "dtype":
+        d.dtype = 7
+    elif bad_desc == "head_dim":
+        d.head_dim = 96
+    elif bad_desc == "block_size":
+        d.block_size = 12
+    elif bad_desc == "null":
+        d = None
+    elif bad_desc == "huge_pool":
+        d.num_blocks = 1 << 27
+    assert decode(d, **kw) == want
+
+
+def test_write_validation():
+    L = B.lib()
+    d = desc()
+    assert L.pa_write_kv(FAKE, FAKE, FAKE, -1, FAKE, FAKE, ctypes.byref(d), None) == B.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_write_kv(None, FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(d), None) == B.PA_ERR_INVALID_ARGUMENT
+    assert L.pa_write_kv(FAKE, FAKE, FAKE, 3, FAKE, FAKE, None, None) == B.PA_ERR_INVALID_ARGUMENT
+    d.head_dim = 80
+    assert L.pa_write_kv(FAKE, FAKE, FAKE, 3, FAKE, FAKE, ctypes.byref(d), None) == B.PA_ERR_UNSUPPORTED
+    # zero tokens: nothing to do, no launch
+    assert L.pa_write_kv(None, None, None, 0, None, None, ctypes.byref(desc()), None) == B.PA_OK
+
+
+def test_zero_sequences_is_a_noop():
+    assert decode(desc(), n=0, q=None, k=FAKE, cl=None, out=None, bt=None, maxlen=0) == B.PA_OK
+
+
+def test_workspace_query():
+    d = desc(hkv=8)
+    assert B.pa_decode_workspace_bytes(256, 32, d, 256) == 0          # one partition
+    got = B.pa_decode_workspace_bytes(256, 32, d, 4096, 256)
+    rows = 256 * 32 * 16
+    ml_off = (rows * 128 * 4 + 255) // 256 * 256
+    assert got == ml_off + rows * 2 * 4
+    assert B.pa_decode_workspace_bytes(256, 31, d, 4096) == 0        # invalid -> 0
