@@ -71,6 +71,8 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
   if (!plan || num_seqs < 0 || num_q_heads <= 0 || max_context_len < 0)
     return PA_ERR_INVALID_ARGUMENT;
   if (num_q_heads % pool->num_kv_heads != 0) return PA_ERR_INVALID_ARGUMENT;
+  // sequences and heads index grid dimensions y/z (at most 65535 each)
+  if (num_seqs > 65535 || num_q_heads > 65535) return PA_ERR_UNSUPPORTED;
   const int32_t group = num_q_heads / pool->num_kv_heads;
   if (!group_supported(group)) return PA_ERR_UNSUPPORTED;
   if (max_blocks_per_seq >= 0 &&

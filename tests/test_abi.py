@@ -48,6 +48,7 @@ def decode(d, **kw):
     (dict(maxlen=8 * 16 + 1), None, B.PA_ERR_INVALID_ARGUMENT),  # > MB * B
     (dict(maxlen=-1), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(n=-1), None, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(n=70000), None, B.PA_ERR_UNSUPPORTED),            # grid limit
     (dict(q=None), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(cl=None), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(out=None), None, B.PA_ERR_INVALID_ARGUMENT),
