@@ -90,11 +90,12 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
                       const pa_pool_desc* pool, void* stream);
 
 /*
- * pa_decode_workspace_bytes -- size in bytes of the float32 workspace that
- * pa_decode needs for these sizes (0 when every sequence fits in a single
- * context partition, in which case workspace may be NULL).  partition_tokens
- * is the context partition length (a multiple of 16), or 0 for the library's
- * choice.  Returns 0 also for invalid sizes (pa_decode reports those).
+ * pa_decode_workspace_bytes -- size in bytes of the scratch buffer pa_decode
+ * needs for these sizes and this partition_tokens (see pa_decode).  With
+ * partition_tokens == 0 and num_seqs <= 2048 the size depends only on the
+ * query heads per kv head and head_dim.  0 means no workspace is needed (a
+ * fixed partition longer than every sequence), and workspace may be NULL.
+ * Returns 0 also for invalid sizes (pa_decode reports those).
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  const pa_pool_desc* pool, int32_t max_context_len,
@@ -123,11 +124,17 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 bytes for the same sizes and partition_tokens; its contents
  *                 on entry do not matter.  Calls sharing one workspace must be
  *                 ordered on one stream.
- *   partition_tokens  context partition length (multiple of 16), or 0 for
- *                 the library's choice.  Sequences longer than one partition
- *                 are split, and the per-partition results are merged by a
- *                 log-sum-exp reduction; the result does not depend on the
- *                 partition length beyond float32 rounding.
+ *   partition_tokens  how the context is split across workgroups:
+ *                 0  -- the library's choice: the flattened work of all
+ *                       (sequence, kv head) pairs, in 16-token tiles, is cut
+ *                       into equal contiguous shares, one per resident
+ *                       workgroup (at most 2048 sequences; above that, fixed
+ *                       256-token partitions);
+ *                 >0 -- fixed context partitions of that many tokens (a
+ *                       multiple of 16, at most 8192).
+ *                 Pieces of a pair computed by different workgroups are
+ *                 merged by log-sum-exp in a second kernel; the result does
+ *                 not depend on the split beyond float32 rounding.
  *
  * Supported: head_dim 64 or 128; query heads per kv head 1..8 or 16.
  */

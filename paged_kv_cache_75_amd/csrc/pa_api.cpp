@@ -56,12 +56,12 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   s = pa::check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out, num_seqs);
   if (s != PA_OK) return s;
   if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0) return PA_OK;
   if (plan.ws_bytes > 0) {
     if (!workspace) return PA_ERR_INVALID_ARGUMENT;
     if (workspace_bytes < plan.ws_bytes) return PA_ERR_WORKSPACE_TOO_SMALL;
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARGUMENT;
   }
-  if (num_seqs == 0) return PA_OK;
 
   pa::DecodeArgs a;
   a.q = q;
@@ -70,10 +70,10 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.out = out;
-  a.ws_o = static_cast<float*>(workspace);
-  a.ws_ml = plan.ws_bytes
-                ? reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.ws_ml_offset)
-                : nullptr;
+  char* ws = static_cast<char*>(workspace);
+  a.ws_o = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_o_offset) : nullptr;
+  a.ws_ml = plan.ws_bytes ? reinterpret_cast<float*>(ws + plan.ws_ml_offset) : nullptr;
+  a.ws_hdr = plan.balanced ? reinterpret_cast<int32_t*>(ws + plan.ws_hdr_offset) : nullptr;
   a.num_seqs = num_seqs;
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = pool->num_kv_heads;
@@ -82,7 +82,8 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.max_context_len = max_context_len;
   a.partition_tokens = plan.partition_tokens;
-  a.num_partitions = plan.num_partitions;
+  a.num_partitions = plan.balanced ? 0 : plan.num_partitions;
+  a.min_split_tiles = pa::kMinSplitTiles;
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   const hipError_t e = pa::launch_decode(a, pool->dtype, pool->head_dim, plan.group,
                                          static_cast<hipStream_t>(stream));

@@ -30,8 +30,13 @@ struct DecodeArgs {
   const int32_t* block_tables;
   const int32_t* context_lens;
   void* out;
-  float* ws_o;              // [num_seqs][num_q_heads][num_partitions][head_dim]
-  float* ws_ml;             // [num_seqs][num_q_heads][num_partitions][2]: max, sum
+  // workspace.  Fixed partitions: ws_o [num_seqs][num_q_heads][num_partitions]
+  // [head_dim], ws_ml [..][num_partitions][2] (max, sum).  Balanced split:
+  // per piece (2 per workgroup) ws_hdr [4] = {valid, seq, kv head, flags},
+  // ws_ml [group][2], ws_o [group][head_dim].
+  float* ws_o;
+  float* ws_ml;
+  int32_t* ws_hdr;
   int32_t num_seqs;
   int32_t num_q_heads;
   int32_t num_kv_heads;
@@ -40,7 +45,8 @@ struct DecodeArgs {
   int32_t max_blocks_per_seq;
   int32_t max_context_len;  // lengths above it are clamped to it
   int32_t partition_tokens;
-  int32_t num_partitions;
+  int32_t num_partitions;   // 0 selects the balanced split
+  int32_t min_split_tiles;  // balanced split: tiles per workgroup share, at least
   float scale_log2;         // scale * log2(e): scores live in the exp2 domain
 };
 

@@ -82,20 +82,29 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
     return PA_ERR_INVALID_ARGUMENT;
   if (partition_tokens > kMaxPartitionTokens) return PA_ERR_UNSUPPORTED;
 
-  const int32_t P = partition_tokens ? partition_tokens : auto_partition(max_context_len);
-  // a partition's block-table slice must fit the LDS copy
-  if (P / pool->block_size + 2 > kTableSliceCap) return PA_ERR_UNSUPPORTED;
-
   DecodePlan p;
   p.group = group;
-  p.partition_tokens = P;
-  p.num_partitions = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
   p.log2_block = ilog2(pool->block_size);
-  if (p.num_partitions > 1) {
-    const size_t rows = size_t(num_seqs) * size_t(num_q_heads) * size_t(p.num_partitions);
-    const size_t o_bytes = rows * size_t(pool->head_dim) * sizeof(float);
-    p.ws_ml_offset = (o_bytes + 255) / 256 * 256;
-    p.ws_bytes = p.ws_ml_offset + rows * 2 * sizeof(float);
+  const size_t D = size_t(pool->head_dim);
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+  if (partition_tokens == 0 && num_seqs <= kMaxSplitSeqs) {
+    // balanced split: two piece slots per workgroup share
+    const size_t pieces = size_t(kMaxSplits) * 2;
+    p.balanced = true;
+    p.ws_hdr_offset = 0;
+    p.ws_ml_offset = align(pieces * 4 * sizeof(int32_t));
+    p.ws_o_offset = align(p.ws_ml_offset + pieces * size_t(group) * 2 * sizeof(float));
+    p.ws_bytes = p.ws_o_offset + pieces * size_t(group) * D * sizeof(float);
+  } else {
+    const int32_t P = partition_tokens ? partition_tokens : auto_partition(max_context_len);
+    p.partition_tokens = P;
+    p.num_partitions = max_context_len > 0 ? (max_context_len + P - 1) / P : 1;
+    if (p.num_partitions > 1) {
+      const size_t rows = size_t(num_seqs) * size_t(num_q_heads) * size_t(p.num_partitions);
+      p.ws_o_offset = 0;
+      p.ws_ml_offset = align(rows * D * sizeof(float));
+      p.ws_bytes = p.ws_ml_offset + rows * 2 * sizeof(float);
+    }
   }
   *plan = p;
   return PA_OK;

@@ -11,10 +11,14 @@ namespace pa {
 
 // Tokens per compute tile: one 16-column MFMA tile of keys.
 constexpr int32_t kTileTokens = 16;
-// Largest block-table slice one decode workgroup stages in LDS.
-constexpr int32_t kTableSliceCap = 1024;
 // Largest context partition.
 constexpr int32_t kMaxPartitionTokens = 8192;
+// Balanced split: at most this many workgroups (shares of the work), at most
+// this many sequences per call, and at least this many 16-token tiles per
+// share (smaller batches use fewer workgroups).
+constexpr int32_t kMaxSplits = 2048;
+constexpr int32_t kMaxSplitSeqs = 2048;
+constexpr int32_t kMinSplitTiles = 32;
 
 int32_t dtype_bytes(int32_t dtype);   // 0 for an unknown dtype
 
@@ -26,11 +30,14 @@ pa_status check_write(const void* k, const void* v, const int32_t* slot_mapping,
 
 struct DecodePlan {
   int32_t group = 0;              // query heads per kv head
-  int32_t partition_tokens = 0;   // tokens per context partition
-  int32_t num_partitions = 0;     // partitions of the longest sequence
+  bool balanced = false;          // balanced split (else fixed partitions)
+  int32_t partition_tokens = 0;   // fixed partitions: tokens per partition
+  int32_t num_partitions = 0;     // fixed partitions: of the longest sequence
   int32_t log2_block = 0;
-  size_t ws_bytes = 0;            // 0 when num_partitions == 1
-  size_t ws_ml_offset = 0;        // byte offset of the (max, sum) pairs
+  size_t ws_bytes = 0;            // 0 when nothing needs merging
+  size_t ws_hdr_offset = 0;       // byte offsets inside the workspace
+  size_t ws_ml_offset = 0;
+  size_t ws_o_offset = 0;
 };
 
 // Shape checks plus the launch plan.  max_blocks_per_seq < 0 skips the

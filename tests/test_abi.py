@@ -57,6 +57,8 @@ def decode(d, **kw):
     (dict(scale=float("nan")), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(maxlen=100, part=16, ws=None), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(maxlen=100, part=16, wsb=16), None, B.PA_ERR_WORKSPACE_TOO_SMALL),
+    (dict(ws=None), None, B.PA_ERR_INVALID_ARGUMENT),              # balanced split needs one
+    (dict(wsb=1 << 16), None, B.PA_ERR_WORKSPACE_TOO_SMALL),
     (dict(), "dtype", B.PA_ERR_INVALID_ARGUMENT),
     (dict(), "head_dim", B.PA_ERR_UNSUPPORTED),
     (dict(), "block_size", B.PA_ERR_UNSUPPORTED),
@@ -96,9 +98,21 @@ def test_zero_sequences_is_a_noop():
 
 def test_workspace_query():
     d = desc(hkv=8)
-    assert B.pa_decode_workspace_bytes(256, 32, d, 256) == 0          # one partition
+    # balanced split (partition_tokens == 0): two pieces per workgroup share,
+    # independent of the batch
+    pieces = 2048 * 2
+    hdr = pieces * 16
+    ml_off = (hdr + 255) // 256 * 256
+    o_off = (ml_off + pieces * 4 * 2 * 4 + 255) // 256 * 256
+    want = o_off + pieces * 4 * 128 * 4
+    assert B.pa_decode_workspace_bytes(256, 32, d, 256) == want
+    assert B.pa_decode_workspace_bytes(7, 32, d, 4096) == want
+    # fixed partitions: one record per (seq, q head, partition); none for one partition
+    assert B.pa_decode_workspace_bytes(256, 32, d, 256, 256) == 0
     got = B.pa_decode_workspace_bytes(256, 32, d, 4096, 256)
     rows = 256 * 32 * 16
-    ml_off = (rows * 128 * 4 + 255) // 256 * 256
-    assert got == ml_off + rows * 2 * 4
+    assert got == (rows * 128 * 4 + 255) // 256 * 256 + rows * 2 * 4
+    # more sequences than the balanced split takes: fixed 256-token partitions
+    rows = 4000 * 32 * 2
+    assert B.pa_decode_workspace_bytes(4000, 32, d, 512) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
     assert B.pa_decode_workspace_bytes(256, 31, d, 4096) == 0        # invalid -> 0
