@@ -47,7 +47,24 @@ def parse():
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 512 MiB buffer 10 times (reference for the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}), flush=True)
 
 
 def cpu_baseline(w, budget_s: float):
@@ -81,6 +98,9 @@ def kv_bytes_per_step(w) -> int:
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
                           "n_gpus": args.gpus}), flush=True)

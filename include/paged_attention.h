@@ -92,8 +92,8 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
 /*
  * pa_decode_workspace_bytes -- size in bytes of the scratch buffer pa_decode
  * needs for these sizes and this partition_tokens (see pa_decode).  With
- * partition_tokens == 0 and num_seqs <= 2048 the size depends only on the
- * query heads per kv head and head_dim.  0 means no workspace is needed (a
+ * partition_tokens == 0, a 16-bit dtype, block_size >= 16 and num_seqs <= 1024
+ * the size depends only on the query heads per kv head and head_dim.  0 means no workspace is needed (a
  * fixed partition longer than every sequence), and workspace may be NULL.
  * Returns 0 also for invalid sizes (pa_decode reports those).
  */
@@ -125,11 +125,12 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *                 on entry do not matter.  Calls sharing one workspace must be
  *                 ordered on one stream.
  *   partition_tokens  how the context is split across workgroups:
- *                 0  -- the library's choice: the flattened work of all
+ *                 0  -- the library's choice: for fp16/bf16 pools with a
+ *                       block size of at least 16, the flattened work of all
  *                       (sequence, kv head) pairs, in 16-token tiles, is cut
- *                       into equal contiguous shares, one per resident
- *                       workgroup (at most 2048 sequences; above that, fixed
- *                       256-token partitions);
+ *                       into equal contiguous shares, one per resident wave
+ *                       (at most 1024 sequences); otherwise fixed 256-token
+ *                       partitions;
  *                 >0 -- fixed context partitions of that many tokens (a
  *                       multiple of 16, at most 8192).
  *                 Pieces of a pair computed by different workgroups are

@@ -13,7 +13,9 @@ import ctypes
 import os
 import re
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libpa.so")
+# PA_LIBRARY selects another build of the same library (A/B measurements)
+LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "_lib", "libpa.so")
 HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                            "include", "paged_attention.h")
 

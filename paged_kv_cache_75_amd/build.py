@@ -30,6 +30,9 @@ SOURCES = ["pa_plan.cpp", "pa_api.cpp", "pa_kernels.hip"]
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in ordinary VGPRs: the softmax rescale touches
+    # them with vector ALU instructions every tile
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
@@ -54,24 +57,25 @@ def _run(cmd, verbose):
         print(out, flush=True)
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: str = LIB_PATH, extra_flags=(), build_dir: str = BUILD_DIR) -> str:
     """Compile every source and link libpa.so; returns the library path."""
     cc = hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    os.makedirs(LIB_DIR, exist_ok=True)
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
 
     def compile_one(src):
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        _run([cc, *COMMON_FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj], verbose)
+        _run([cc, *COMMON_FLAGS, *extra_flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
         return obj
 
     with ThreadPoolExecutor(len(SOURCES)) as ex:
         objs = list(ex.map(compile_one, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

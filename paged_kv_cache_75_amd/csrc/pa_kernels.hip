@@ -22,8 +22,13 @@ namespace pa {
 namespace {
 
 constexpr int kWave = 64;
-constexpr int kDecodeWaves = 4;
-constexpr int kDecodeThreads = kWave * kDecodeWaves;
+// raw buffer descriptor, word 3 for gfx9-family chips: 32-bit data format,
+// no swizzle; loads past num_records return zero
+constexpr int kBufferDword3 = 0x00020000;
+// fixed partitions: four waves share one partition (the balanced split runs
+// one wave per workgroup: each wave is its own share of the work)
+constexpr int kPartitionWaves = 4;
+constexpr int kMergeThreads = 256;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -83,6 +88,35 @@ template <> __device__ inline void store_elem<PA_BF16>(void* base, size_t idx, f
     r = static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
   }
   static_cast<uint16_t*>(base)[idx] = r;
+}
+
+// four consecutive outputs (one 8- or 16-byte store)
+template <int DT> __device__ inline void store4(void* base, int64_t idx, f32x4 x);
+template <> __device__ inline void store4<PA_F32>(void* base, int64_t idx, f32x4 x) {
+  *reinterpret_cast<f32x4*>(static_cast<float*>(base) + idx) = x;
+}
+template <> __device__ inline void store4<PA_F16>(void* base, int64_t idx, f32x4 x) {
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+  const h4 h = {static_cast<_Float16>(x[0]), static_cast<_Float16>(x[1]),
+                static_cast<_Float16>(x[2]), static_cast<_Float16>(x[3])};
+  *reinterpret_cast<h4*>(static_cast<_Float16*>(base) + idx) = h;
+}
+template <> __device__ inline void store4<PA_BF16>(void* base, int64_t idx, f32x4 x) {
+  uint16_t* p = static_cast<uint16_t*>(base) + idx;
+  uint32_t w[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    uint16_t h[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t u = __float_as_uint(x[2 * i + j]);
+      h[j] = ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
+                 ? static_cast<uint16_t>((u >> 16) | 0x0040u)
+                 : static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    }
+    w[i] = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
+  }
+  *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
 }
 
 // ---------------------------------------------------------------------------
@@ -199,118 +233,262 @@ struct Geo {
   static_assert(CPR % 4 == 0 && kWave % CPR == 0 && kTileTokens % RPI == 0, "shape");
 };
 
-template <int DT, int D, int G>
-struct SegmentSmem {
-  f32x4 p[kDecodeWaves][kTileTokens][Geo<DT, D, G>::NHB];
-  float m[kDecodeWaves][G];
-  float l[kDecodeWaves][G];
-  float o[kDecodeWaves][G][D];
+template <int DT, int D>
+struct KeyRegs {
+  uint4 k[Geo<DT, D, 1>::KK];
+};
+template <int DT, int D>
+struct ValRegs {
+  uint4 v[Geo<DT, D, 1>::VS];
 };
 
-// Attend over tiles [tile_lo, tile_hi) (at least one) of pair (seq, g) whose
-// sequence holds T > 0 tokens.  Ends with a workgroup barrier after which
-// sm.m / sm.l / sm.o hold every wave's max, sum and unnormalised output.
-template <int DT, int D, int G, bool kTileInBlock>
-__device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G>& sm, int seq, int g,
-                               int T, int tile_lo, int tile_hi) {
-  using GE = Geo<DT, D, G>;
-  constexpr int EPC = GE::EPC, CPR = GE::CPR, KK = GE::KK, RPI = GE::RPI, VS = GE::VS;
-  constexpr int NHB = GE::NHB, kRowBytes = GE::kRowBytes;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int gq = lane >> 4;
-  const int c = lane & 15;
-  const int rho = lane / CPR;
-  const int chi = lane % CPR;
-  const int Hq = a.num_q_heads;
-  const int hq0 = g * G;
+// ---------------------------------------------------------------------------
+// Tile math for 16-bit elements: both products on the matrix cores.
+//   Scores transposed, S^T = K . Q^T: A = the key tile (row = token c, as
+//   loaded), B = Q^T (column = query head c; columns >= G are zero).  Lane
+//   (gq, c) gets tokens 4gq..4gq+3 of head c, so the softmax of a head lives
+//   in the four lanes c, c+16, c+32, c+48.
+//   Output transposed, O^T += V^T . P^T: B = P^T is exactly the lane's four
+//   probabilities (rounded to the element type); A = V^T comes from the
+//   wave's V tile in LDS through the gfx950 transpose read, which hands lane
+//   (gq, r) the values V[4gq..4gq+3][16n + r].  V rows are stored with their
+//   16-byte chunks XOR-swizzled per row so that neither the row writes nor the
+//   transposed reads hit the same LDS bank twice.
+// ---------------------------------------------------------------------------
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef _Float16 v4f16 __attribute__((ext_vector_type(4)));
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
-  // query A operands: row c carries head 4*hb + (c & 3); heads >= G are zero
-  uint4 qa[NHB][KK];
-#pragma unroll
-  for (int hb = 0; hb < NHB; ++hb) {
-    const int head = 4 * hb + (c & 3);
-    const int head_ld = head < G ? head : G - 1;   // padding rows never dereference
-    const uint4* qrow = reinterpret_cast<const uint4*>(
-        static_cast<const char*>(a.q) + (int64_t(seq) * Hq + hq0 + head_ld) * kRowBytes);
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      qa[hb][kk] = head < G ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+template <int DT> __device__ inline f32x4 mfma_pv(v4i16 a, v4i16 b, f32x4 acc);
+template <> __device__ inline f32x4 mfma_pv<PA_BF16>(v4i16 a, v4i16 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, acc, 0, 0, 0);
+}
+template <> __device__ inline f32x4 mfma_pv<PA_F16>(v4i16 a, v4i16 b, f32x4 acc) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(v4f16, a),
+                                               __builtin_bit_cast(v4f16, b), acc, 0, 0, 0);
+}
+
+template <int DT> __device__ inline v4i16 pack4(const float* p);
+template <> __device__ inline v4i16 pack4<PA_BF16>(const float* p) {
+  const v4bf16 x = {static_cast<__bf16>(p[0]), static_cast<__bf16>(p[1]),
+                    static_cast<__bf16>(p[2]), static_cast<__bf16>(p[3])};
+  return __builtin_bit_cast(v4i16, x);
+}
+template <> __device__ inline v4i16 pack4<PA_F16>(const float* p) {
+  const v4f16 x = {static_cast<_Float16>(p[0]), static_cast<_Float16>(p[1]),
+                   static_cast<_Float16>(p[2]), static_cast<_Float16>(p[3])};
+  return __builtin_bit_cast(v4i16, x);
+}
+
+template <int DT, int D, int G>
+struct MfmaPv {
+  using GE = Geo<DT, D, G>;
+  static constexpr int KK = GE::KK, VS = GE::VS, RPI = GE::RPI, CPR = GE::CPR;
+  static constexpr int kRowBytes = GE::kRowBytes;
+  static constexpr int NT = D / 16;                       // 16-row output tiles of O^T
+  static constexpr int kRowsPer256 = 256 / kRowBytes;     // rows sharing one bank sweep
+  static constexpr int kScratchBytes = kTileTokens * kRowBytes;   // the wave's V tile
+  static_assert(G <= 16, "at most 16 query heads per kv head");
+
+  uint4 qb[KK];
+  f32x4 o[NT];
+  float m_run, l_run;
+  int gq, c, rho, chi;
+
+  __device__ static int swz(int t) { return (2 * (t / kRowsPer256)) & (CPR - 1); }
+
+  __device__ void set_lane(int lane) {
+    gq = lane >> 4;
+    c = lane & 15;
+    rho = lane / CPR;
+    chi = lane % CPR;
   }
 
-  const int lb = a.log2_block;
-  const int bmask = (1 << lb) - 1;
-  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
-  const int64_t head_rows = int64_t(g) << lb;                 // kv head g inside a block
-  const int64_t blk_rows = int64_t(a.num_kv_heads) << lb;     // rows per block
-  const char* kbase = static_cast<const char*>(a.k_pool);
-  const char* vbase = static_cast<const char*>(a.v_pool);
-  const int nblk = a.num_blocks;
+  __device__ void reset() {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    m_run = -INFINITY;
+    l_run = 0.0f;
+  }
 
-  const int span = tile_hi - tile_lo - wave;
-  const int nmine = span > 0 ? (span + kDecodeWaves - 1) / kDecodeWaves : 0;
+  // query rows of the pair from global memory ([G][D] contiguous at qrows)
+  __device__ void init(const DecodeArgs& a, int seq, int g, int lane) {
+    set_lane(lane);
+    const int head = c < G ? c : G - 1;          // padding columns never dereference
+    const uint4* qrow = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(a.q) +
+        (int64_t(seq) * a.num_q_heads + int64_t(g) * G + head) * kRowBytes);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = c < G ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+    reset();
+  }
 
-  // block ids of this wave's tiles, 64 tiles per load: lane j holds the block
-  // of the wave's tile 64*batch + j (used when a tile lies inside one block)
-  int tbl = 0;
-  auto load_tbl = [&](int batch) {
-    const int k = min(64 * batch + lane, nmine - 1);
-    const int t = min((tile_lo + wave + kDecodeWaves * k) * kTileTokens, T - 1);
-    tbl = min(max(table[t >> lb], 0), nblk - 1);
-  };
+  // query rows of the pair from an LDS copy ([G][D])
+  __device__ void load_q_lds(const char* qs) {
+    const int head = c < G ? c : 0;
+    const uint4* qrow = reinterpret_cast<const uint4*>(qs + head * kRowBytes);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qb[kk] = c < G ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+  }
 
-  struct Regs {
-    uint4 k[KK];
-    uint4 v[VS];
-  };
-  // Tokens past T-1 (the tail of the sequence's last tile) read row T-1: finite
-  // data, never a slot outside the sequence; their probability is zero.
-  auto load_tile = [&](int kidx, Regs& r) {
-    const int t0 = (tile_lo + wave + kDecodeWaves * kidx) * kTileTokens;
-    const int last = T - 1 - t0;
-    if constexpr (kTileInBlock) {
-      const int64_t blk = __builtin_amdgcn_readlane(tbl, kidx & 63);
-      const int64_t row0 = blk * blk_rows + head_rows + (t0 & bmask);
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + (row0 + min(c, last)) * kRowBytes);
+  float p_[4];
+  float alpha_;
+
+  // phase 1: the value tile goes to LDS (chunks swizzled per row)
+  __device__ void stage_values(const ValRegs<DT, D>& r, char* vt) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) r.k[kk] = kp[4 * kk + gq];
-#pragma unroll
-      for (int s = 0; s < VS; ++s)
-        r.v[s] = reinterpret_cast<const uint4*>(
-            vbase + (row0 + min(s * RPI + rho, last)) * kRowBytes)[chi];
-    } else {
-      auto row_of = [&](int dt) -> int64_t {
-        const int t = t0 + min(dt, last);
-        const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
-        return blk * blk_rows + head_rows + (t & bmask);
-      };
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + row_of(c) * kRowBytes);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) r.k[kk] = kp[4 * kk + gq];
-#pragma unroll
-      for (int s = 0; s < VS; ++s)
-        r.v[s] = reinterpret_cast<const uint4*>(vbase + row_of(s * RPI + rho) * kRowBytes)[chi];
+    for (int s = 0; s < VS; ++s) {
+      const int row = s * RPI + rho;
+      *reinterpret_cast<uint4*>(vt + row * kRowBytes + ((chi ^ swz(row)) << 4)) = r.v[s];
     }
-  };
+  }
 
-  float m_run[NHB][4], l_run[NHB][4];
+  // phase 2: S^T = K . Q^T, rows >= live masked, online softmax update
+  __device__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
+    f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+    for (int kk = 0; kk < KK; ++kk) sc = mfma_chunk<DT>(r.k[kk], qb[kk], sc);
+    float s[4];
+    float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      m_run[hb][i] = -INFINITY;
-      l_run[hb][i] = 0.0f;
+      s[i] = 4 * gq + i < live ? sc[i] * a.scale_log2 : -INFINITY;
+      mx = fmaxf(mx, s[i]);
     }
-  float acc[G][EPC];
+    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = m_new == -INFINITY ? 0.0f : m_new;
+    alpha_ = __builtin_amdgcn_exp2f(m_run - m_use);
+    float psum = 0.0f;
 #pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
+    for (int i = 0; i < 4; ++i) {
+      p_[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+      psum += p_[i];
+    }
+    l_run = fmaf(l_run, alpha_, psum);
+    m_run = m_new;
+  }
 
-  auto compute_tile = [&](int kidx, const Regs& r) {
-    const int t0 = (tile_lo + wave + kDecodeWaves * kidx) * kTileTokens;
-    const bool valid = t0 + c < T;
-    float pr[NHB][4], alpha[NHB][4];
+  // phase 3: O^T = alpha O^T + V^T . P^T
+  __device__ void accumulate(const char* vt) {
+#pragma unroll
+    for (int n = 0; n < NT; ++n) o[n] *= alpha_;
+    const v4i16 pb = pack4<DT>(p_);
+    wave_sync_lds();
+    // A operand of tile n: lane (gq, r) points at V[4gq + r/4][16n + 4(r%4)]
+    const int row = 4 * gq + (c >> 2);
+    const char* rbase = vt + row * kRowBytes + ((c & 1) << 3);
+    const int sw = swz(row);
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int chunk = 2 * n + ((c & 3) >> 1);
+      const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_v4i16*)(rbase + ((chunk ^ sw) << 4)));
+      o[n] = mfma_pv<DT>(av, pb, o[n]);
+    }
+    wave_sync_lds();
+  }
+
+  // One wave holds the whole segment: write its result from registers.
+  // complete: out rows (row0 + c) get O/l; otherwise the piece slot gets
+  // O/l, the running max and the sum.  Lane (gq, c < G) owns d = 16n+4gq+i.
+  __device__ void store_result(const DecodeArgs& a, int64_t row0, bool complete, int piece) {
+    float l = l_run;
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (c >= G) return;
+    const float inv = 1.0f / l;
+    if (complete) {
+#pragma unroll
+      for (int n = 0; n < NT; ++n) store4<DT>(a.out, (row0 + c) * D + 16 * n + 4 * gq, o[n] * inv);
+    } else {
+      float* po = a.ws_o + (int64_t(piece) * G + c) * D;
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+        *reinterpret_cast<f32x4*>(po + 16 * n + 4 * gq) = o[n] * inv;
+      if (gq == 0) {
+        a.ws_ml[(piece * G + c) * 2] = m_run;
+        a.ws_ml[(piece * G + c) * 2 + 1] = l;
+      }
+    }
+  }
+
+  // wave totals into sm: O^T lane (gq, c), element i of tile n = head c, d = 16n + 4gq + i
+  template <typename Smem>
+  __device__ void finish(Smem& sm, int wave) {
+    float l = l_run;
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (c < G) {
+      if (gq == 0) {
+        sm.m[wave][c] = m_run;
+        sm.l[wave][c] = l;
+      }
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sm.o[wave][c][16 * n + 4 * gq + i] = o[n][i];
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Tile math for float32 elements: QK^T on the float32 matrix cores with the
+// query heads repeated down the 16 rows (lane (gq, c) gets token c's scores
+// for four heads), softmax reductions across the 16 token lanes by DPP, and
+// P.V on the vector ALUs: lane (rho, chi) accumulates chunk chi of its value
+// rows for every head, reading the probabilities from a per-wave LDS tile.
+// ---------------------------------------------------------------------------
+template <int DT, int D, int G>
+struct ValuPv {
+  using GE = Geo<DT, D, G>;
+  static constexpr int EPC = GE::EPC, KK = GE::KK, VS = GE::VS, RPI = GE::RPI, CPR = GE::CPR;
+  static constexpr int NHB = GE::NHB, kRowBytes = GE::kRowBytes;
+  static constexpr int kScratchBytes = kTileTokens * NHB * 16;   // probabilities
+
+  uint4 qa[NHB][KK];
+  float m_run[NHB][4], l_run[NHB][4];
+  float acc[G][EPC];
+  int gq, c, rho, chi;
+
+  __device__ void init(const DecodeArgs& a, int seq, int g, int lane) {
+    gq = lane >> 4;
+    c = lane & 15;
+    rho = lane / CPR;
+    chi = lane % CPR;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      const int head = 4 * hb + (c & 3);
+      const int head_ld = head < G ? head : G - 1;
+      const uint4* qrow = reinterpret_cast<const uint4*>(
+          static_cast<const char*>(a.q) +
+          (int64_t(seq) * a.num_q_heads + int64_t(g) * G + head_ld) * kRowBytes);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        qa[hb][kk] = head < G ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        m_run[hb][i] = -INFINITY;
+        l_run[hb][i] = 0.0f;
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[h][e] = 0.0f;
+  }
+
+  ValRegs<DT, D> vals_;
+  float pr_[NHB][4];
+  f32x4* sp_ = nullptr;
+
+  __device__ void stage_values(const ValRegs<DT, D>& r, char*) { vals_ = r; }
+
+  __device__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
+    const bool valid = c < live;
+    float alpha[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
       f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -322,8 +500,8 @@ __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G>& sm, i
         const float m_new = fmaxf(m_run[hb][i], row_max16(s));
         const float m_use = m_new == -INFINITY ? 0.0f : m_new;
         alpha[hb][i] = __builtin_amdgcn_exp2f(m_run[hb][i] - m_use);
-        pr[hb][i] = __builtin_amdgcn_exp2f(s - m_use);
-        l_run[hb][i] = l_run[hb][i] * alpha[hb][i] + pr[hb][i];
+        pr_[hb][i] = __builtin_amdgcn_exp2f(s - m_use);
+        l_run[hb][i] = l_run[hb][i] * alpha[hb][i] + pr_[hb][i];
         m_run[hb][i] = m_new;
       }
     }
@@ -331,21 +509,24 @@ __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G>& sm, i
     for (int h = 0; h < G; ++h)
 #pragma unroll
       for (int e = 0; e < EPC; ++e) acc[h][e] *= alpha[h / 4][h % 4];
+  }
 
+  __device__ void accumulate(char* scratch) {
+    f32x4* sp = reinterpret_cast<f32x4*>(scratch);        // [16 tokens][NHB]
     if (gq == 0) {
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb)
-        sm.p[wave][c][hb] = f32x4{pr[hb][0], pr[hb][1], pr[hb][2], pr[hb][3]};
+        sp[c * NHB + hb] = f32x4{pr_[hb][0], pr_[hb][1], pr_[hb][2], pr_[hb][3]};
     }
     wave_sync_lds();
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
       float v[EPC];
-      unpack<DT>(r.v[s], v);
+      unpack<DT>(vals_.v[s], v);
       const int row = s * RPI + rho;
 #pragma unroll
       for (int hb = 0; hb < NHB; ++hb) {
-        const f32x4 pp = sm.p[wave][row][hb];
+        const f32x4 pp = sp[row * NHB + hb];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int h = 4 * hb + i;
@@ -357,69 +538,197 @@ __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G>& sm, i
       }
     }
     wave_sync_lds();
-  };
-
-  if (nmine > 0) {
-    if constexpr (kTileInBlock) load_tbl(0);
-    Regs A, B;
-    load_tile(0, A);
-    for (int k = 0; k < nmine; k += 2) {
-      if (k + 1 < nmine) {
-        if (kTileInBlock && ((k + 1) & 63) == 0) load_tbl((k + 1) >> 6);
-        load_tile(k + 1, B);
-      }
-      compute_tile(k, A);
-      if (k + 1 >= nmine) break;
-      if (k + 2 < nmine) {
-        if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
-        load_tile(k + 2, A);
-      }
-      compute_tile(k + 1, B);
-    }
   }
 
-  // wave totals: l summed over the 16 token lanes, acc over the value rows
+  template <typename Smem>
+  __device__ void finish(Smem& sm, int wave) {
 #pragma unroll
-  for (int hb = 0; hb < NHB; ++hb)
+    for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) l_run[hb][i] = row_sum16(l_run[hb][i]);
-#pragma unroll
-  for (int h = 0; h < G; ++h)
-#pragma unroll
-    for (int e = 0; e < EPC; ++e) {
-      float x = acc[h][e];
-#pragma unroll
-      for (int w = CPR; w < kWave; w <<= 1) x += __shfl_xor(x, w, kWave);
-      acc[h][e] = x;
-    }
-  if (lane == 0) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      sm.m[wave][h] = m_run[h / 4][h % 4];
-      sm.l[wave][h] = l_run[h / 4][h % 4];
-    }
-  }
-  if (rho == 0) {
+      for (int i = 0; i < 4; ++i) l_run[hb][i] = row_sum16(l_run[hb][i]);
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPC; ++e) sm.o[wave][h][chi * EPC + e] = acc[h][e];
+      for (int e = 0; e < EPC; ++e) {
+        float x = acc[h][e];
+#pragma unroll
+        for (int w = CPR; w < kWave; w <<= 1) x += __shfl_xor(x, w, kWave);
+        acc[h][e] = x;
+      }
+    if (gq == 0 && c == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        sm.m[wave][h] = m_run[h / 4][h % 4];
+        sm.l[wave][h] = l_run[h / 4][h % 4];
+      }
+    }
+    if (rho == 0) {
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) sm.o[wave][h][chi * EPC + e] = acc[h][e];
+    }
   }
+};
+
+template <int DT, int D, int G>
+struct TileMathFor {
+  using type = MfmaPv<DT, D, G>;
+};
+template <int D, int G>
+struct TileMathFor<PA_F32, D, G> {
+  using type = ValuPv<PA_F32, D, G>;
+};
+
+template <int DT, int D, int G, int NW>
+struct SegmentSmem {
+  static constexpr int kScratch = TileMathFor<DT, D, G>::type::kScratchBytes;
+  alignas(16) char scratch[NW][kScratch];
+  float m[NW][G];
+  float l[NW][G];
+  float o[NW][G][D];
+};
+
+// Attend over tiles [tile_lo, tile_hi) (at least one) of pair (seq, g) whose
+// sequence holds T > 0 tokens.  Ends with a workgroup barrier after which
+// sm.m / sm.l / sm.o hold every wave's max, sum and unnormalised output.
+template <int DT, int D, int G, bool kTileInBlock, int NW>
+__device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G, NW>& sm, int seq, int g,
+                               int T, int tile_lo, int tile_hi) {
+  // the segment is the same for every lane; say so, so that addresses and
+  // buffer descriptors derived from it stay in scalar registers
+  seq = __builtin_amdgcn_readfirstlane(seq);
+  g = __builtin_amdgcn_readfirstlane(g);
+  T = __builtin_amdgcn_readfirstlane(T);
+  tile_lo = __builtin_amdgcn_readfirstlane(tile_lo);
+  tile_hi = __builtin_amdgcn_readfirstlane(tile_hi);
+  using GE = Geo<DT, D, G>;
+  constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
+  constexpr int kRowBytes = GE::kRowBytes;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int gq = lane >> 4;
+  const int c = lane & 15;
+  const int rho = lane / CPR;
+  const int chi = lane % CPR;
+
+  typename TileMathFor<DT, D, G>::type tm;
+  tm.init(a, seq, g, lane);
+
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
+  const int64_t head_rows = int64_t(g) << lb;                 // kv head g inside a block
+  const int64_t blk_rows = int64_t(a.num_kv_heads) << lb;     // rows per block
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int nblk = a.num_blocks;
+
+  const int span = tile_hi - tile_lo - wave;
+  const int nmine = span > 0 ? (span + NW - 1) / NW : 0;
+
+  // block ids of this wave's tiles, 64 tiles per load: lane j holds the block
+  // of the wave's tile 64*batch + j (used when a tile lies inside one block)
+  int tbl = 0;
+  auto load_tbl = [&](int batch) {
+    const int k = min(64 * batch + lane, nmine - 1);
+    const int t = min((tile_lo + wave + NW * k) * kTileTokens, T - 1);
+    tbl = min(max(table[t >> lb], 0), nblk - 1);
+  };
+
+  // per-lane byte offsets inside a tile's 16 rows (constant for the segment)
+  const int k_off = c * kRowBytes + gq * 16;          // key chunk gq of row c; +64 per kk
+  const int v_off = rho * kRowBytes + chi * 16;       // value chunk chi of row rho
+  auto tile_start = [&](int kidx) { return (tile_lo + wave + NW * kidx) * kTileTokens; };
+  auto tile_byte = [&](int kidx, int t0) -> int64_t {
+    const int64_t blk = __builtin_amdgcn_readlane(tbl, kidx & 63);
+    return (blk * blk_rows + head_rows + (t0 & bmask)) * kRowBytes;
+  };
+  // The tile's 16 rows are contiguous inside one (block, kv head) run: a
+  // buffer descriptor spans exactly the live rows, so rows past T-1 (the tail
+  // of the sequence's last tile) load as zeros and are never read.
+  auto rsrc = [&](const char* base, int64_t byte, int t0) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + byte), 0,
+                                             min(kTileTokens, T - t0) * kRowBytes, kBufferDword3);
+  };
+  // Without that (blocks smaller than a tile) each lane finds its own block;
+  // tokens past T-1 read row T-1 (finite data of this sequence, weight zero).
+  auto row_of = [&](int t0, int dt) -> int64_t {
+    const int t = t0 + min(dt, T - 1 - t0);
+    const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
+    return blk * blk_rows + head_rows + (t & bmask);
+  };
+  auto load_keys = [&](int kidx, KeyRegs<DT, D>& r) {
+    const int t0 = tile_start(kidx);
+    if constexpr (kTileInBlock) {
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, tile_byte(kidx, t0), t0);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        r.k[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
+    } else {
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + row_of(t0, c) * kRowBytes);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) r.k[kk] = kp[4 * kk + gq];
+    }
+  };
+  auto load_values = [&](int kidx, ValRegs<DT, D>& r) {
+    const int t0 = tile_start(kidx);
+    if constexpr (kTileInBlock) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_byte(kidx, t0), t0);
+#pragma unroll
+      for (int s = 0; s < VS; ++s)
+        r.v[s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rv, v_off + s * RPI * kRowBytes, 0, 0));
+    } else {
+#pragma unroll
+      for (int s = 0; s < VS; ++s)
+        r.v[s] = reinterpret_cast<const uint4*>(vbase + row_of(t0, s * RPI + rho) * kRowBytes)[chi];
+    }
+  };
+
+  char* scratch = sm.scratch[wave];
+  // Keys are double-buffered in registers; values are single-buffered: the
+  // next tile's values are requested as soon as this tile's are in LDS.
+  if (nmine > 0) {
+    if constexpr (kTileInBlock) load_tbl(0);
+    KeyRegs<DT, D> KA, KB;
+    ValRegs<DT, D> VR;
+    load_keys(0, KA);
+    load_values(0, VR);
+    if (nmine > 1) load_keys(1, KB);
+    auto step = [&](int k, KeyRegs<DT, D>& kr) {
+      tm.stage_values(VR, scratch);
+      if (k + 1 < nmine) load_values(k + 1, VR);
+      tm.scores(a, kr, min(kTileTokens, T - tile_start(k)));
+      if (k + 2 < nmine) {
+        if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
+        load_keys(k + 2, kr);
+      }
+      tm.accumulate(scratch);
+    };
+    for (int k = 0; k < nmine; k += 2) {
+      step(k, KA);
+      if (k + 1 >= nmine) break;
+      step(k + 1, KB);
+    }
+  }
+  // a wave without tiles reports m = -inf, l = 0, o = 0
+  tm.finish(sm, wave);
   __syncthreads();
 }
 
 // Merge the four waves' results for (head h, element d): M = max, L = sum of
 // 2^(m_w - M) l_w, O = sum of 2^(m_w - M) o_w.  The attention output is O / L.
-template <int DT, int D, int G>
-__device__ inline void merge_waves(const SegmentSmem<DT, D, G>& sm, int h, int d, float& M,
+template <int DT, int D, int G, int NW>
+__device__ inline void merge_waves(const SegmentSmem<DT, D, G, NW>& sm, int h, int d, float& M,
                                    float& L, float& O) {
   M = sm.m[0][h];
 #pragma unroll
-  for (int w = 1; w < kDecodeWaves; ++w) M = fmaxf(M, sm.m[w][h]);
+  for (int w = 1; w < NW; ++w) M = fmaxf(M, sm.m[w][h]);
   L = 0.0f;
   O = 0.0f;
 #pragma unroll
-  for (int w = 0; w < kDecodeWaves; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float f = __builtin_amdgcn_exp2f(sm.m[w][h] - M);
     L = fmaf(f, sm.l[w][h], L);
     O = fmaf(f, sm.o[w][h][d], O);
@@ -428,49 +737,85 @@ __device__ inline void merge_waves(const SegmentSmem<DT, D, G>& sm, int h, int d
 
 template <int DT, int D>
 __device__ inline void zero_rows(const DecodeArgs& a, int64_t row0, int nrows) {
-  for (int i = threadIdx.x; i < nrows * D; i += kDecodeThreads)
+  for (int i = threadIdx.x; i < nrows * D; i += blockDim.x)
     store_elem<DT>(a.out, row0 * D + i, 0.0f);
 }
 
 // ---------------------------------------------------------------------------
-// Balanced split (the default).  The grid holds as many workgroups as the GPU
-// keeps resident.  The flattened work (sequence, kv head, tile) is cut into
-// equal contiguous shares, one per workgroup, so long and short sequences
-// load every workgroup alike.  A pair cut by a share boundary leaves one
-// "piece" per workgroup it touches: (max, sum, normalised output) per head in
-// slot 0 (the share's first segment) or slot 1 (its last), and the piece
-// merge kernel combines them.  Pairs inside one share are written directly.
+// Balanced split (the default for 16-bit elements and blocks of >= 16
+// tokens).  The grid holds as many one-wave workgroups as the GPU keeps
+// resident.  The flattened work (sequence, kv head, 16-token tile) is cut
+// into equal contiguous shares, one per wave, so long and short sequences
+// load every wave alike.
+//
+// A wave lists the (sequence, kv head) segments of its share (up to kSegCap
+// at a time), copies their query rows to LDS and computes, 64 tiles per
+// register batch, each tile's byte offset in the pools and its number of live
+// rows.  It then streams the tiles without draining at segment boundaries:
+// keys are requested two tiles ahead, values one tile ahead.  A segment that
+// covers its whole pair is written to the output directly; a pair cut by a
+// share boundary leaves a "piece" (max, sum, normalised output per head) in
+// slot 0 (the share's first segment) or slot 1 (its last); the first piece
+// also records how many shares the pair spans, and the piece merge kernel
+// combines them.
 // ---------------------------------------------------------------------------
 constexpr int kPieceFirst = 1;   // the piece starts at the pair's first tile
 constexpr int kPieceLast = 2;    // the piece ends at the pair's last tile
+constexpr int kHdrInts = 8;      // valid, seq, kv head, flags, pieces, (pad)
+constexpr int kQStageBytes = 8192;
 
-template <int DT, int D, int G, bool kTileInBlock>
-__global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs a) {
-  __shared__ SegmentSmem<DT, D, G> sm;
-  __shared__ int32_t s_len[kMaxSplitSeqs];
-  __shared__ long long s_wsum[kDecodeWaves];
-  __shared__ long long s_start[2];
+constexpr int kPairCost = 1;
+
+__device__ inline int pair_units(int T) {
+  const int tiles = (T + kTileTokens - 1) / kTileTokens;
+  return tiles ? tiles + kPairCost : 0;
+}
+
+template <int DT, int D, int G>
+struct StreamSmem {
+  static constexpr int kQBytes = G * D * 2;
+  static constexpr int kSegCap = std::max(2, std::min(16, kQStageBytes / kQBytes));
+  alignas(16) char vtile[MfmaPv<DT, D, G>::kScratchBytes];
+  alignas(16) char q[kSegCap][kQBytes];
+  int32_t len[kMaxSplitSeqs];
+  int32_t seg_seq[kSegCap];
+  int32_t seg_g[kSegCap];
+  int32_t seg_tile0[kSegCap];
+  int32_t seg_start[kSegCap];
+  int32_t seg_n[kSegCap];
+  int32_t seg_flags[kSegCap];
+  int32_t seg_pieces[kSegCap];
+};
+
+template <int DT, int D, int G>
+__global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
+  using GE = Geo<DT, D, G>;
+  using SM = StreamSmem<DT, D, G>;
+  constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
+  constexpr int kRowBytes = GE::kRowBytes;
+  __shared__ SM sm;
 
   const int w = blockIdx.x;
   const int W = gridDim.x;
   const int N = a.num_seqs;
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int wave = tid / kWave;
+  const int lane = threadIdx.x;
 
-  if (tid < 2) a.ws_hdr[(2 * w + tid) * 4] = 0;   // both piece slots empty so far
+  if (lane < 2) a.ws_hdr[(2 * w + lane) * kHdrInts] = 0;   // both piece slots empty so far
 
-  // clamped lengths into LDS; tiles of this thread's run of sequences
-  const int chunk = (N + kDecodeThreads - 1) / kDecodeThreads;
-  const int i0 = min(N, tid * chunk);
+  // clamped lengths into LDS; tiles of this lane's run of sequences; prefix
+  const int chunk = (N + kWave - 1) / kWave;
+  const int i0 = min(N, lane * chunk);
   const int i1 = min(N, i0 + chunk);
+  // Work is measured in units: a (sequence, kv head) pair of n tiles costs
+  // n + kPairCost units, the extra ones standing for the fixed cost of a
+  // segment (query rows, the partial last tile, the result store).
   long long mine = 0;
   for (int i = i0; i < i1; ++i) {
     const int T = min(max(a.context_lens[i], 0), a.max_context_len);
-    s_len[i] = T;
-    mine += (T + kTileTokens - 1) / kTileTokens;
+    sm.len[i] = T;
+    mine += pair_units(T);
   }
   long long incl = mine;
 #pragma unroll
@@ -478,126 +823,249 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_split_kernel(DecodeArgs
     const long long y = __shfl_up(incl, o, kWave);
     if (lane >= o) incl += y;
   }
-  if (lane == kWave - 1) s_wsum[wave] = incl;
-  __syncthreads();
-  long long before = 0, all_tiles = 0;
-#pragma unroll
-  for (int i = 0; i < kDecodeWaves; ++i) {
-    before += i < wave ? s_wsum[i] : 0;
-    all_tiles += s_wsum[i];
-  }
-  const long long excl = before + incl - mine;
+  const long long all_units = __shfl(incl, kWave - 1, kWave);
+  const long long excl = incl - mine;
+  wave_sync_lds();
 
   // zero-length sequences get zero rows (spread over every workgroup)
   for (int s = w; s < N; s += W)
-    if (s_len[s] == 0) zero_rows<DT, D>(a, int64_t(s) * Hq, Hq);
+    if (sm.len[s] == 0) zero_rows<DT, D>(a, int64_t(s) * Hq, Hq);
 
-  const long long total = all_tiles * Hkv;
+  const long long total = all_units * Hkv;
   const long long want = (total + a.min_split_tiles - 1) / a.min_split_tiles;
-  const int Weff = int(max(1LL, min(static_cast<long long>(W), want)));
+  const long long Weff = max(1LL, min(static_cast<long long>(W), want));
   if (w >= Weff) return;
   const long long lo = total * w / Weff;
   const long long hi = total * (w + 1) / Weff;
   if (lo >= hi) return;
-  if (mine > 0 && lo >= excl * Hkv && lo < (excl + mine) * Hkv) {
-    long long cum = excl;
-    for (int i = i0; i < i1; ++i) {
-      const int t = (s_len[i] + kTileTokens - 1) / kTileTokens;
-      if (lo < (cum + t) * Hkv) {
-        s_start[0] = i;
-        s_start[1] = cum;
-        break;
-      }
-      cum += t;
-    }
-  }
-  __syncthreads();
+  // the lane whose run of sequences holds tile lo
+  const bool holds = mine > 0 && lo >= excl * Hkv && lo < (excl + mine) * Hkv;
+  const unsigned long long holders = __ballot(holds);
+  if (holders == 0) return;          // unreachable for lo < total
+  const int first = __builtin_ctzll(holders);
+  int s = __builtin_amdgcn_readfirstlane(first * chunk);
+  long long cum = __shfl(excl, first, kWave);
 
-  int s = int(s_start[0]);
-  long long cum = s_start[1];
+  MfmaPv<DT, D, G> tm;
+  tm.set_lane(lane);
+  const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
+  const int k_off = c * kRowBytes + gq * 16;          // key chunk gq of row c; +64 per kk
+  const int v_off = rho * kRowBytes + chi * 16;       // value chunk chi of row rho
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
+  const int64_t blk_rows = int64_t(Hkv) << lb;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+
   long long pos = lo;
   while (pos < hi && s < N) {
-    const int T = s_len[s];
-    const int tiles = (T + kTileTokens - 1) / kTileTokens;
-    const long long base = cum * Hkv;
-    if (pos >= base + static_cast<long long>(tiles) * Hkv) {
-      cum += tiles;
-      ++s;
-      continue;
-    }
-    const long long r = pos - base;
-    const int g = int(r / tiles);
-    const int tile0 = int(r - static_cast<long long>(g) * tiles);
-    const long long seg_end = min(hi, base + static_cast<long long>(g + 1) * tiles);
-    const int tile1 = tile0 + int(seg_end - pos);
-    attend_segment<DT, D, G, kTileInBlock>(a, sm, s, g, T, tile0, tile1);
-
-    const int flags = (tile0 == 0 ? kPieceFirst : 0) | (tile1 == tiles ? kPieceLast : 0);
-    const int64_t row0 = int64_t(s) * Hq + int64_t(g) * G;
-    if (flags == (kPieceFirst | kPieceLast)) {
-      for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
-        const int h = idx / D, d = idx - (idx / D) * D;
-        float M, L, O;
-        merge_waves(sm, h, d, M, L, O);
-        store_elem<DT>(a.out, (row0 + h) * D + d, O / L);
+    // ---- the next run of segments (uniform walk over LDS lengths) ----
+    int nseg = 0, ntot = 0;
+    while (pos < hi && s < N && nseg < SM::kSegCap) {
+      const int T = __builtin_amdgcn_readfirstlane(sm.len[s]);
+      const int units = pair_units(T);
+      const int tiles = units - (units ? kPairCost : 0);
+      const long long base = cum * Hkv;
+      if (pos >= base + static_cast<long long>(units) * Hkv) {
+        cum += units;
+        ++s;
+        continue;
       }
-    } else {
-      const int piece = 2 * w + (pos == lo ? 0 : 1);
-      for (int idx = tid; idx < G * D; idx += kDecodeThreads) {
-        const int h = idx / D, d = idx - (idx / D) * D;
-        float M, L, O;
-        merge_waves(sm, h, d, M, L, O);
-        a.ws_o[(int64_t(piece) * G + h) * D + d] = O / L;
-        if (d == 0) {
-          a.ws_ml[(piece * G + h) * 2] = M;
-          a.ws_ml[(piece * G + h) * 2 + 1] = L;
+      // pos - base < Hkv * units, below 2^31 (the plan checks it)
+      const int r = int(pos - base);
+      const int g = r / units;
+      const long long pair_start = base + static_cast<long long>(g) * units;
+      const long long pair_end = pair_start + units;
+      const long long seg_end = min(hi, pair_end);
+      // the pair's first kPairCost units carry no tiles
+      const int tile0 = max(0, int(pos - pair_start) - kPairCost);
+      const int tile1 = int(seg_end - pair_start) - kPairCost;
+      if (tile1 <= tile0) {           // this share holds none of the pair's tiles
+        pos = seg_end;
+        continue;
+      }
+      const int n = tile1 - tile0;
+      int flags = (tile0 == 0 ? kPieceFirst : 0) | (tile1 == tiles ? kPieceLast : 0);
+      // shares spanned by the pair: this one up to the one holding its last unit
+      const long long w_last = (pair_end * Weff - 1) / total;
+      if (lane == 0) {
+        sm.seg_seq[nseg] = s;
+        sm.seg_g[nseg] = g;
+        sm.seg_tile0[nseg] = tile0;
+        sm.seg_start[nseg] = ntot;
+        sm.seg_n[nseg] = n;
+        sm.seg_flags[nseg] = flags | (pos == lo ? 0 : 4);
+        sm.seg_pieces[nseg] = int(w_last - w + 1);
+      }
+      ntot += n;
+      ++nseg;
+      pos = seg_end;
+    }
+    wave_sync_lds();
+
+    // ---- query rows of these segments into LDS ----
+    constexpr int kQChunks = SM::kQBytes / 16;
+    for (int idx = lane; idx < nseg * kQChunks; idx += kWave) {
+      const int sg = idx / kQChunks;
+      const int part = idx - sg * kQChunks;
+      const uint4* src = reinterpret_cast<const uint4*>(
+          static_cast<const char*>(a.q) +
+          (int64_t(sm.seg_seq[sg]) * Hq + int64_t(sm.seg_g[sg]) * G) * kRowBytes);
+      *reinterpret_cast<uint4*>(sm.q[sg] + part * 16) = src[part];
+    }
+
+    // ---- per-tile descriptors, 64 tiles per batch: lane j holds tile
+    //      64*batch + j: its first row's byte offset and (segment, live rows)
+    int64_t doff = 0;
+    int dmeta = 0;
+    auto load_batch = [&](int batch) {
+      const int j = min(64 * batch + lane, ntot - 1);
+      int sg = 0;
+      for (int i = 1; i < nseg; ++i)
+        if (j >= sm.seg_start[i]) sg = i;
+      const int seq = sm.seg_seq[sg];
+      const int t0 = (sm.seg_tile0[sg] + j - sm.seg_start[sg]) * kTileTokens;
+      const int T = sm.len[seq];
+      const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
+      const int64_t blk = min(max(table[t0 >> lb], 0), a.num_blocks - 1);
+      doff = (blk * blk_rows + (int64_t(sm.seg_g[sg]) << lb) + (t0 & bmask)) * kRowBytes;
+      dmeta = min(kTileTokens, T - t0) | (sg << 8);
+    };
+    auto tile_off = [&](int k) -> int64_t {
+      const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff), k & 63);
+      const uint32_t hi32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff >> 32), k & 63);
+      return (int64_t(hi32) << 32) | lo32;
+    };
+    auto tile_meta = [&](int k) -> int { return __builtin_amdgcn_readlane(dmeta, k & 63); };
+    // a tile's rows are contiguous in one (block, kv head) run; the descriptor
+    // spans the live rows only, so rows past a sequence's end load as zeros
+    auto rsrc = [&](const char* base, int64_t off, int live) {
+      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0,
+                                               live * kRowBytes, kBufferDword3);
+    };
+    struct Keys {
+      KeyRegs<DT, D> r;
+      int meta;
+    };
+    auto load_keys = [&](int k, Keys& kr) {
+      if ((k & 63) == 0 && k > 0) load_batch(k >> 6);
+      const int meta = tile_meta(k);
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, tile_off(k), meta & 0xff);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kr.r.k[kk] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
+      kr.meta = meta;
+    };
+    ValRegs<DT, D> vr;
+    auto load_vals = [&](int k) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_off(k), tile_meta(k) & 0xff);
+#pragma unroll
+      for (int s2 = 0; s2 < VS; ++s2)
+        vr.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 rv, v_off + s2 * RPI * kRowBytes, 0, 0));
+    };
+
+    load_batch(0);
+    wave_sync_lds();                 // the query rows are in LDS
+    Keys KA, KB;
+    load_keys(0, KA);
+    load_vals(0);
+    if (ntot > 1) load_keys(1, KB);
+    int cur = -1;
+    auto step = [&](int k, Keys& kr) {
+      const int sg = kr.meta >> 8;
+      if (sg != cur) {               // a new segment begins
+        cur = sg;
+        tm.reset();
+        tm.load_q_lds(sm.q[sg]);
+      }
+      tm.stage_values(vr, sm.vtile);
+      if (k + 1 < ntot) load_vals(k + 1);
+      tm.scores(a, kr.r, kr.meta & 0xff);
+      if (k + 2 < ntot) load_keys(k + 2, kr);
+      tm.accumulate(sm.vtile);
+      if (k + 1 == sm.seg_start[sg] + sm.seg_n[sg]) {   // the segment's last tile
+        const int flags = sm.seg_flags[sg];
+        const bool complete = (flags & 3) == (kPieceFirst | kPieceLast);
+        const int piece = 2 * w + ((flags & 4) ? 1 : 0);
+        const int seq = sm.seg_seq[sg];
+        const int g = sm.seg_g[sg];
+        tm.store_result(a, int64_t(seq) * Hq + int64_t(g) * G, complete, piece);
+        if (!complete && lane == 0) {
+          int32_t* hdr = a.ws_hdr + piece * kHdrInts;
+          hdr[1] = seq;
+          hdr[2] = g;
+          hdr[3] = flags & 3;
+          hdr[4] = sm.seg_pieces[sg];
+          hdr[0] = 1;
         }
       }
-      if (tid == 0) {
-        int32_t* hdr = a.ws_hdr + piece * 4;
-        hdr[1] = s;
-        hdr[2] = g;
-        hdr[3] = flags;
-        hdr[0] = 1;
-      }
+    };
+    for (int k = 0; k < ntot; k += 2) {
+      step(k, KA);
+      if (k + 1 >= ntot) break;
+      step(k + 1, KB);
     }
-    __syncthreads();       // sm is reused by the next segment
-    pos = seg_end;
+    wave_sync_lds();                 // LDS records are rewritten by the next run
   }
 }
 
-// Combine the pieces of every pair that starts inside this workgroup's share
-// and continues into the next shares (slot 0 of the following workgroups,
-// up to the piece that holds the pair's last tile).
+// Combine the pieces of every pair that starts inside this share: the piece
+// here (slot 0 or 1) and slot 0 of the next pieces-1 shares.  One wave per
+// share; lane t owns float4 quads t, t+64, ... of the pair's [G][D] output.
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void merge_pieces_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave) void merge_pieces_kernel(DecodeArgs a, int W) {
   const int w = blockIdx.x;
-  const int W = gridDim.x;
+  constexpr int kQuads = G * D / 4;
   for (int slot = 0; slot < 2; ++slot) {
-    const int32_t* hdr = a.ws_hdr + (2 * w + slot) * 4;
-    if (hdr[0] == 0 || (hdr[3] & kPieceFirst) == 0) continue;
-    const int seq = hdr[1];
-    const int g = hdr[2];
+    const int32_t* hdr = a.ws_hdr + (2 * w + slot) * kHdrInts;
+    if (__builtin_amdgcn_readfirstlane(hdr[0]) == 0 ||
+        (__builtin_amdgcn_readfirstlane(hdr[3]) & kPieceFirst) == 0)
+      continue;
+    const int seq = __builtin_amdgcn_readfirstlane(hdr[1]);
+    const int g = __builtin_amdgcn_readfirstlane(hdr[2]);
+    const int np = min(__builtin_amdgcn_readfirstlane(hdr[4]), W - w);
     const int64_t row0 = int64_t(seq) * a.num_q_heads + int64_t(g) * G;
-    for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
-      const int h = idx / D, d = idx - (idx / D) * D;
-      float M = -INFINITY, L = 0.0f, O = 0.0f;
-      int piece = 2 * w + slot;
-      for (int ww = w; ww < W; ++ww) {
-        const float m = a.ws_ml[(piece * G + h) * 2];
-        const float l = a.ws_ml[(piece * G + h) * 2 + 1];
-        const float o = a.ws_o[(int64_t(piece) * G + h) * D + d];
-        const int fl = a.ws_hdr[piece * 4 + 3];
-        const float M2 = fmaxf(M, m);
-        const float f_old = __builtin_amdgcn_exp2f(M - M2);
-        const float f_new = l * __builtin_amdgcn_exp2f(m - M2);
-        L = L * f_old + f_new;
-        O = O * f_old + f_new * o;
-        M = M2;
-        if (fl & kPieceLast) break;
-        piece = 2 * (ww + 1);
+    for (int qd = threadIdx.x; qd < kQuads; qd += kWave) {
+      const int h = qd / (D / 4);
+      // pieces are read kBatch at a time (all loads in flight together) and
+      // folded into a running (M, L, O) with the usual rescale
+      constexpr int kBatch = 8;
+      float M = -INFINITY, L = 0.0f;
+      f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int p0 = 0; p0 < np; p0 += kBatch) {
+        float m[kBatch], l[kBatch];
+        f32x4 o[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int p = p0 + j;
+          if (p < np) {
+            const int piece = p == 0 ? 2 * w + slot : 2 * (w + p);
+            m[j] = a.ws_ml[(piece * G + h) * 2];
+            l[j] = a.ws_ml[(piece * G + h) * 2 + 1];
+            o[j] = reinterpret_cast<const f32x4*>(a.ws_o + int64_t(piece) * G * D)[qd];
+          } else {
+            m[j] = -INFINITY;
+            l[j] = 0.0f;
+            o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          }
+        }
+        float Mb = M;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, m[j]);
+        const float f = __builtin_amdgcn_exp2f(M - Mb);
+        L *= f;
+        O *= f;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const float wgt = l[j] * __builtin_amdgcn_exp2f(m[j] - Mb);
+          L += wgt;
+          O += wgt * o[j];
+        }
+        M = Mb;
       }
-      store_elem<DT>(a.out, (row0 + h) * D + d, O / L);
+      store4<DT>(a.out, row0 * D + 4 * qd, O * (1.0f / L));
     }
   }
 }
@@ -608,8 +1076,9 @@ __global__ __launch_bounds__(kDecodeThreads) void merge_pieces_kernel(DecodeArgs
 // partition and lse_reduce_kernel merges them.
 // ---------------------------------------------------------------------------
 template <int DT, int D, int G, bool kTileInBlock>
-__global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(DecodeArgs a) {
-  __shared__ SegmentSmem<DT, D, G> sm;
+__global__ __launch_bounds__(kWave * kPartitionWaves) void decode_partition_kernel(DecodeArgs a) {
+  constexpr int NW = kPartitionWaves;
+  __shared__ SegmentSmem<DT, D, G, NW> sm;
   const int part = blockIdx.x;
   const int g = blockIdx.y;
   const int seq = blockIdx.z;
@@ -626,8 +1095,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
   if (lo >= tiles) return;
   const int hi = min(tiles, lo + tpp);
   const int nparts = (tiles + tpp - 1) / tpp;
-  attend_segment<DT, D, G, kTileInBlock>(a, sm, seq, g, T, lo, hi);
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+  attend_segment<DT, D, G, kTileInBlock, NW>(a, sm, seq, g, T, lo, hi);
+  for (int idx = threadIdx.x; idx < G * D; idx += kWave * NW) {
     const int h = idx / D, d = idx - (idx / D) * D;
     float M, L, O;
     merge_waves(sm, h, d, M, L, O);
@@ -647,7 +1116,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_partition_kernel(Decode
 // log-sum-exp merge of the partitions of one (sequence, kv head) pair:
 //   M = max_p m_p,  w_p = l_p 2^(m_p - M),  out = sum_p w_p o_p / sum_p w_p
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kDecodeThreads) void lse_reduce_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a) {
   const int g = blockIdx.x;
   const int seq = blockIdx.y;
   const int T = min(a.context_lens[seq], a.max_context_len);
@@ -655,7 +1124,7 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_reduce_kernel(DecodeArgs a
   const int nparts = T > 0 ? (T + P - 1) / P : 0;
   if (nparts <= 1) return;
   const int NP = a.num_partitions;
-  for (int idx = threadIdx.x; idx < G * D; idx += kDecodeThreads) {
+  for (int idx = threadIdx.x; idx < G * D; idx += kMergeThreads) {
     const int h = idx / D, d = idx - (idx / D) * D;
     const int64_t row = int64_t(seq) * a.num_q_heads + int64_t(g) * G + h;
     const float* ml = a.ws_ml + 2 * row * NP;
@@ -678,7 +1147,7 @@ __global__ __launch_bounds__(kDecodeThreads) void lse_reduce_kernel(DecodeArgs a
 // launch
 // ---------------------------------------------------------------------------
 // Workgroups of `kernel` the device keeps resident at once (cached per device).
-int resident_workgroups(const void* kernel, int kernel_id) {
+int resident_workgroups(const void* kernel, int kernel_id, int threads) {
   static std::mutex mu;
   static std::map<std::pair<int, int>, int> cache;
   int dev = 0;
@@ -690,7 +1159,7 @@ int resident_workgroups(const void* kernel, int kernel_id) {
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kDecodeThreads, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) !=
       hipSuccess)
     return 0;
   const int n = std::min(kMaxSplits, std::max(1, cus * std::max(1, per_cu)));
@@ -698,34 +1167,37 @@ int resident_workgroups(const void* kernel, int kernel_id) {
   return n;
 }
 
-template <int DT, int D, int G, bool kTileInBlock>
-hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_partitions == 0) {          // balanced split
-    const void* k = reinterpret_cast<const void*>(&decode_split_kernel<DT, D, G, kTileInBlock>);
-    const int W = resident_workgroups(k, (DT * 1000 + D) * 100 + G * 2 + (kTileInBlock ? 1 : 0));
-    if (W <= 0) return hipErrorInvalidDevice;
-    hipLaunchKernelGGL((decode_split_kernel<DT, D, G, kTileInBlock>), dim3(W),
-                       dim3(kDecodeThreads), 0, stream, a);
-    hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W), dim3(kDecodeThreads), 0,
-                       stream, a);
+template <int DT, int D, int G>
+hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
+  if (a.num_partitions == 0) {
+    // balanced split: 16-bit elements, tiles inside one block (checked by the plan)
+    if constexpr (DT == PA_F32) {
+      return hipErrorInvalidValue;
+    } else {
+      const void* k = reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G>);
+      const int W = resident_workgroups(k, (DT * 1000 + D) * 100 + G, kWave);
+      if (W <= 0) return hipErrorInvalidDevice;
+      hipLaunchKernelGGL((decode_stream_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a);
+      hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a,
+                         W);
+    }
   } else {
     const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
-    hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, kTileInBlock>), grid,
-                       dim3(kDecodeThreads), 0, stream, a);
+    // a 16-token tile lies inside one block when the block size is a multiple of 16
+    if (a.log2_block >= 4) {
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, true>), grid,
+                         dim3(kWave * kPartitionWaves), 0, stream, a);
+    } else {
+      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, false>), grid,
+                         dim3(kWave * kPartitionWaves), 0, stream, a);
+    }
     if (a.num_partitions > 1) {
       const dim3 rgrid(a.num_kv_heads, a.num_seqs);
-      hipLaunchKernelGGL((lse_reduce_kernel<DT, D, G>), rgrid, dim3(kDecodeThreads), 0,
+      hipLaunchKernelGGL((lse_reduce_kernel<DT, D, G>), rgrid, dim3(kMergeThreads), 0,
                          stream, a);
     }
   }
   return hipGetLastError();
-}
-
-template <int DT, int D, int G>
-hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-  // a 16-token tile lies inside one block when the block size is a multiple of 16
-  if (a.log2_block >= 4) return launch_decode_t<DT, D, G, true>(a, stream);
-  return launch_decode_t<DT, D, G, false>(a, stream);
 }
 
 template <int DT, int D>

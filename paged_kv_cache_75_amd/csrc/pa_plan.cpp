@@ -87,12 +87,18 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
   p.log2_block = ilog2(pool->block_size);
   const size_t D = size_t(pool->head_dim);
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
-  if (partition_tokens == 0 && num_seqs <= kMaxSplitSeqs) {
-    // balanced split: two piece slots per workgroup share
+  // balanced split: 16-bit elements (matrix-core P.V), blocks holding whole
+  // 16-token tiles, and a batch whose lengths fit the kernel's LDS copy
+  // (the kernel indexes one sequence's work, kv heads x (tiles + 1), in 32 bits)
+  const int64_t seq_units =
+      int64_t(pool->num_kv_heads) * (max_context_len / kTileTokens + 2);
+  if (partition_tokens == 0 && num_seqs <= kMaxSplitSeqs && pool->dtype != PA_F32 &&
+      pool->block_size >= kTileTokens && seq_units < (int64_t{1} << 31)) {
+    // two piece slots per workgroup share; an 8-int header per piece
     const size_t pieces = size_t(kMaxSplits) * 2;
     p.balanced = true;
     p.ws_hdr_offset = 0;
-    p.ws_ml_offset = align(pieces * 4 * sizeof(int32_t));
+    p.ws_ml_offset = align(pieces * 8 * sizeof(int32_t));
     p.ws_o_offset = align(p.ws_ml_offset + pieces * size_t(group) * 2 * sizeof(float));
     p.ws_bytes = p.ws_o_offset + pieces * size_t(group) * D * sizeof(float);
   } else {

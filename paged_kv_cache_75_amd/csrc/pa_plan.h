@@ -16,9 +16,9 @@ constexpr int32_t kMaxPartitionTokens = 8192;
 // Balanced split: at most this many workgroups (shares of the work), at most
 // this many sequences per call, and at least this many 16-token tiles per
 // share (smaller batches use fewer workgroups).
-constexpr int32_t kMaxSplits = 2048;
-constexpr int32_t kMaxSplitSeqs = 2048;
-constexpr int32_t kMinSplitTiles = 32;
+constexpr int32_t kMaxSplits = 4096;
+constexpr int32_t kMaxSplitSeqs = 1024;
+constexpr int32_t kMinSplitTiles = 16;
 
 int32_t dtype_bytes(int32_t dtype);   // 0 for an unknown dtype
 

@@ -100,8 +100,8 @@ def test_workspace_query():
     d = desc(hkv=8)
     # balanced split (partition_tokens == 0): two pieces per workgroup share,
     # independent of the batch
-    pieces = 2048 * 2
-    hdr = pieces * 16
+    pieces = 4096 * 2
+    hdr = pieces * 32
     ml_off = (hdr + 255) // 256 * 256
     o_off = (ml_off + pieces * 4 * 2 * 4 + 255) // 256 * 256
     want = o_off + pieces * 4 * 128 * 4
@@ -113,6 +113,6 @@ def test_workspace_query():
     rows = 256 * 32 * 16
     assert got == (rows * 128 * 4 + 255) // 256 * 256 + rows * 2 * 4
     # more sequences than the balanced split takes: fixed 256-token partitions
-    rows = 4000 * 32 * 2
-    assert B.pa_decode_workspace_bytes(4000, 32, d, 512) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
+    rows = 1500 * 32 * 2
+    assert B.pa_decode_workspace_bytes(1500, 32, d, 512) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
     assert B.pa_decode_workspace_bytes(256, 31, d, 4096) == 0        # invalid -> 0
