@@ -90,6 +90,26 @@ def cpu_baseline(w, budget_s: float):
     return bytes_done / secs / 1e12, sample, 1
 
 
+PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama3-8b-bf16.json")
+
+
+def profiled_traffic(cfg):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when it does not describe the kernel
+    as built now (the summary records the kernel source's sha256)."""
+    import hashlib
+    if cfg != 3 or not os.path.exists(PROFILE_SUMMARY):
+        return None, None
+    with open(PROFILE_SUMMARY) as f:
+        prof = json.load(f)
+    src = os.path.join(ROOT, "paged_kv_cache_75_amd", "csrc", "pa_kernels.hip")
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if sha != prof.get("kernel_source_sha256"):
+        return None, None
+    return prof["traffic_bytes_per_launch"], prof
+
+
 def kv_bytes_per_step(w) -> int:
     """Algorithmic KV bytes of one decode step: every cached token's K and V
     row, once per kv head."""
@@ -178,6 +198,8 @@ def main():
     achieved = kv_bytes / (decode_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
 
+    traffic_bytes, prof = profiled_traffic(cfg)
+    traffic = None if traffic_bytes is None else round(traffic_bytes)
     result = {
         "metric": "paged decode attention: KV bytes read/s (TB/s), % HBM peak, us/step",
         "value": round(value, 4),
@@ -206,12 +228,14 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode (partition kernel + log-sum-exp merge)",
+            "kernel": "pa_decode call: decode_stream_kernel + merge_pieces_kernel",
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": traffic,
+            "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
+            "traffic_source": os.path.relpath(PROFILE_SUMMARY, ROOT) if traffic is not None else None,
             "decode_us_mean": round(decode_ms_mean * 1e3, 2),
             "decode_us_min": round(min(decode_ms) * 1e3, 2),
         },
