@@ -243,3 +243,38 @@ def test_empty_batch_and_zero_lengths():
     res = pa_decode(empty, dw.k_pool, dw.v_pool, dw.block_tables[:0], dw.context_lens[:0],
                     0.1, max_context_len=0)
     assert res.shape == (0, 8, 128)
+
+
+def test_workspace_reused_across_calls():
+    """Consecutive calls share one workspace: A, then B (same shapes, other
+    values), then a smaller batch, then A again.  Each result matches the
+    oracle and A's two results are bit-identical, so nothing a call leaves in
+    the workspace (pieces, pair counters) reaches the next one."""
+    import torch
+    from paged_kv_cache_75_amd import (pa_decode, pa_decode_workspace_bytes, pa_write_kv,
+                                       pool_desc)
+    wa = workloads.make(3, seed=1100, num_seqs=128)
+    wb = workloads.make(3, seed=1101, num_seqs=128)
+    da, db = upload(wa, DEV), upload(wb, DEV)
+    for d in (da, db):
+        pa_write_kv(d.new_k, d.new_v, d.slot_mapping, d.k_pool, d.v_pool)
+    T = max(wa.max_context_len, wb.max_context_len)
+    need = pa_decode_workspace_bytes(128, wa.num_q_heads, pool_desc(da.k_pool), T)
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+
+    def run(dw, n=None):
+        n = dw.q.shape[0] if n is None else n
+        return pa_decode(dw.q[:n], dw.k_pool, dw.v_pool, dw.block_tables[:n],
+                         dw.context_lens[:n], dw.scale, max_context_len=T, workspace=ws)
+
+    say("[workspace] A, B, A[:37], A on one workspace")
+    outs = [to_host(run(da), "bf16"), to_host(run(db), "bf16"), to_host(run(da, 37), "bf16"),
+            to_host(run(da), "bf16")]
+    _sync()
+    want_a = oracle_step(wa)[0]
+    want_b = oracle_step(wb)[0]
+    f64 = lambda a: ref.to_float64(a, "bf16")
+    compare(f64(outs[0]), want_a, "bf16", label="A")
+    compare(f64(outs[1]), want_b, "bf16", label="B")
+    compare(f64(outs[2]), want_a[:37], "bf16", label="A[:37]")
+    assert np.array_equal(_bytes(outs[0]), _bytes(outs[3]))
