@@ -2,12 +2,15 @@
 
     python bench.py [--steps K] [--warmup W] [--config 3] [--gpus 1]
 
-One step is the whole hot path for one decode batch: pa_write_kv of the
-batch's new tokens, then pa_decode (the partitioned attention kernel and,
-when a sequence spans several partitions, the log-sum-exp merge).  Inputs are
-resident in HBM before timing starts.  To keep the timed reads cold in the
-GPU caches, steps rotate over several copies of the pools (together well above
-the 256 MB Infinity Cache).
+One step is the whole hot path for one decode batch.  Where the batch writes
+new tokens (configurations 3 and 5) that is pa_append_decode: each sequence's
+newest K/V rows go into the pools and the attention reads them, in one call
+(the stream kernel plus the piece merge, which also writes the rows).  The
+same step as two calls, pa_write_kv then pa_decode, is timed beside it and
+reported as "two_call".  Other configurations decode only (pa_decode).
+Inputs are resident in HBM before timing starts.  To keep the timed reads
+cold in the GPU caches, steps rotate over several copies of the pools
+(together well above the 256 MB Infinity Cache).
 
 Printed: one JSON line with the metric (KV bytes read per second, TB/s), the
 roofline of the decode call measured with HIP events on its stream, and the
@@ -44,6 +47,9 @@ def parse():
     ap.add_argument("--config", type=int, default=3)
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
+    ap.add_argument("--step", choices=("both", "append", "two-call"), default="both",
+                    help="where the batch writes new tokens: time pa_append_decode (headline) "
+                         "and pa_write_kv + pa_decode (both), or only one of them")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -130,8 +136,8 @@ def main():
     import torch
 
     import workloads
-    from paged_kv_cache_75_amd import (pa_decode, pa_decode_workspace_bytes, pa_write_kv,
-                                       pool_desc)
+    from paged_kv_cache_75_amd import (pa_append_decode, pa_decode, pa_decode_workspace_bytes,
+                                       pa_write_kv, pool_desc)
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -163,37 +169,63 @@ def main():
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     writes = cfg in (3, 5)
 
-    def step(k):
-        kp, vp = pools[k % reps]
-        if writes:
-            pa_write_kv(nk, nv, slots, kp, vp)
+    def decode(kp, vp):
         pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
                   workspace=ws, partition_tokens=args.partition)
 
-    for k in range(args.warmup):
-        step(k)
-    torch.cuda.synchronize()
+    def append_decode(kp, vp):
+        pa_append_decode(q, nk, nv, kp, vp, bt, cl, w.scale, out=out,
+                         max_context_len=w.max_context_len, workspace=ws,
+                         partition_tokens=args.partition)
+
+    def timed(pre, call):
+        """Step time: K steps between device synchronisations, nothing else
+        on the stream.  Call time: K more steps with HIP events on the stream
+        around `call` (the decode call) in each; an event record costs the
+        stream a few microseconds, so the two loops are kept apart."""
+        for k in range(args.warmup):
+            kp, vp = pools[k % reps]
+            pre(kp, vp)
+            call(kp, vp)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for k in range(args.steps):
+            kp, vp = pools[k % reps]
+            pre(kp, vp)
+            call(kp, vp)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        stream = torch.cuda.current_stream()
+        for k in range(args.steps):
+            kp, vp = pools[k % reps]
+            pre(kp, vp)
+            ev[k][0].record(stream)
+            call(kp, vp)
+            ev[k][1].record(stream)
+        torch.cuda.synchronize()
+        return (t1 - t0) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in ev]
+
+    def write(kp, vp):
+        pa_write_kv(nk, nv, slots, kp, vp)
+
+    def nothing(kp, vp):
+        pass
 
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(K)]
-    stream = torch.cuda.current_stream()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for k in range(K):
-        kp, vp = pools[k % reps]
-        if writes:
-            pa_write_kv(nk, nv, slots, kp, vp)
-        ev[k][0].record(stream)
-        pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
-                  workspace=ws, partition_tokens=args.partition)
-        ev[k][1].record(stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
+    fused = writes and args.step != "two-call"
+    two_call = writes and args.step != "append"
+    if two_call:
+        two_ms, two_decode_ms = timed(write, decode)
+    if fused:
+        ms_per_step, decode_ms = timed(nothing, append_decode)
+    elif writes:
+        ms_per_step, decode_ms = two_ms, two_decode_ms
+    else:
+        ms_per_step, decode_ms = timed(nothing, decode)
 
     kv_bytes = kv_bytes_per_step(w)
-    ms_per_step = (t1 - t0) * 1e3 / K
-    decode_ms = [a.elapsed_time(b) for a, b in ev]
     decode_ms_mean = sum(decode_ms) / len(decode_ms)
     achieved = kv_bytes / (decode_ms_mean * 1e-3) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
@@ -225,10 +257,13 @@ def main():
             "new_tokens_written": int((w.slot_mapping >= 0).sum()) if writes else 0,
             "pool_copies_rotated": reps,
             "partition_tokens": args.partition or "auto",
+            "step_calls": ("pa_append_decode" if fused else
+                           "pa_write_kv + pa_decode" if writes else "pa_decode"),
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "pa_decode call: decode_stream_kernel + merge_pieces_kernel",
+            "kernel": (("pa_append_decode" if fused else "pa_decode") +
+                       " call: decode_stream_kernel + merge_pieces_kernel"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -240,6 +275,13 @@ def main():
             "decode_us_min": round(min(decode_ms) * 1e3, 2),
         },
     }
+    if two_call and fused:
+        result["two_call"] = {
+            "calls": "pa_write_kv + pa_decode",
+            "us_per_step": round(two_ms * 1e3, 2),
+            "value": round(kv_bytes / (two_ms * 1e-3) / 1e12, 4),
+            "decode_us_mean": round(sum(two_decode_ms) / len(two_decode_ms) * 1e3, 2),
+        }
     if not args.no_cpu_baseline:
         v, sample, cores = cpu_baseline(w, args.cpu_seconds)
         result["cpu_baseline"] = {"value": round(v, 6), "unit": "TB/s", "cores": cores,

@@ -146,6 +146,38 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
                     int32_t partition_tokens, void* stream);
 
+/*
+ * pa_append_decode -- one whole decode step in one call: every sequence's
+ * newest token is placed in the pools and then attended over, with the same
+ * result as
+ *   pa_write_kv(new_k, new_v, slot_mapping, num_seqs, ...), then pa_decode(...)
+ * where slot_mapping[i] is the slot of token T_i - 1 of sequence i (the slot
+ * write and the block-table lookup of the same page as above; the newest
+ * token counts in T_i).  Arguments are those of pa_decode, plus
+ *
+ *   new_k, new_v  [num_seqs][num_kv_heads][head_dim], pool element type: the
+ *                 K and V rows of token T_i - 1 of sequence i.  Rows of
+ *                 sequences with T_i == 0 are ignored.
+ *   k_pool, v_pool  written: token T_i - 1's rows go to block
+ *                 block_tables[i][(T_i - 1) / B] at offset (T_i - 1) % B; an
+ *                 entry outside [0, num_blocks) skips that write.
+ *
+ * Contract: the slot of token T_i - 1 is read by no other sequence of the
+ * call (a block being appended to is private to its sequence).  On the
+ * balanced split the decode takes the newest rows straight from new_k / new_v
+ * and the workgroup that attends over a sequence's last tile also stores
+ * them, so the step is two kernels instead of three; with fixed partitions
+ * the rows are written first and the decode follows.  Workspace:
+ * pa_decode_workspace_bytes.
+ */
+pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
+                           void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                           const int32_t* block_tables, int32_t max_blocks_per_seq,
+                           const int32_t* context_lens, int32_t num_seqs,
+                           int32_t max_context_len, int32_t num_q_heads, float scale,
+                           void* out, void* workspace, size_t workspace_bytes,
+                           int32_t partition_tokens, void* stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_string(pa_status status);
 

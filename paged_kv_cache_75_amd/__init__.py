@@ -2,6 +2,7 @@
 
     pa_write_kv(k, v, slot_mapping, k_pool, v_pool)
     pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, ...)
+    pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, ...)
 
 The functions marshal torch tensors into libpa.so (built in-tree by
 ``paged_kv_cache_75_amd.build``).  They raise RuntimeError when the library is
@@ -9,10 +10,10 @@ missing; nothing falls back to another implementation.
 """
 from .binding import (PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED,
                       PA_ERR_WORKSPACE_TOO_SMALL, PA_F16, PA_F32, PA_OK, PaError, lib,
-                      pa_decode, pa_decode_workspace_bytes, pa_pool_desc, pa_status_string,
-                      pa_write_kv, pool_desc)
+                      pa_append_decode, pa_decode, pa_decode_workspace_bytes, pa_pool_desc,
+                      pa_status_string, pa_write_kv, pool_desc)
 
 __all__ = ["PA_BF16", "PA_ERR_HIP", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED",
            "PA_ERR_WORKSPACE_TOO_SMALL", "PA_F16", "PA_F32", "PA_OK", "PaError", "lib",
-           "pa_decode", "pa_decode_workspace_bytes", "pa_pool_desc", "pa_status_string",
-           "pa_write_kv", "pool_desc"]
+           "pa_append_decode", "pa_decode", "pa_decode_workspace_bytes", "pa_pool_desc",
+           "pa_status_string", "pa_write_kv", "pool_desc"]

@@ -67,6 +67,9 @@ def lib():
     L.pa_decode.argtypes = [vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
                             vp, vp, sz, i32, vp]
     L.pa_decode.restype = ctypes.c_int
+    L.pa_append_decode.argtypes = [vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
+                                   ctypes.c_float, vp, vp, sz, i32, vp]
+    L.pa_append_decode.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -155,6 +158,22 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
     read from the device (a synchronizing copy).  ``workspace`` is a uint8 or
     float32 device tensor of at least pa_decode_workspace_bytes(...) bytes;
     when omitted a fresh one is taken from torch's caching allocator."""
+    return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
+                   max_context_len, workspace, partition_tokens, stream)
+
+
+def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,
+                     out=None, max_context_len=None, workspace=None,
+                     partition_tokens: int = 0, stream=None):
+    """Write token T_i - 1 of every sequence (rows of new_k / new_v,
+    [N][Hkv][D]) into the pools through the block tables and decode, in one
+    call; same result as pa_write_kv followed by pa_decode."""
+    return _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, out,
+                   max_context_len, workspace, partition_tokens, stream)
+
+
+def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, out,
+            max_context_len, workspace, partition_tokens, stream):
     torch = _torch()
     desc = pool_desc(k_pool)
     dev = k_pool.device
@@ -177,17 +196,28 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
     _check(out, "out", dtype=q.dtype, device=dev)
     if tuple(out.shape) != tuple(q.shape):
         raise ValueError("out must have q's shape")
+    if new_k is not None:
+        want = (n, desc.num_kv_heads, desc.head_dim)
+        for t, name in ((new_k, "new_k"), (new_v, "new_v")):
+            _check(t, name, dtype=k_pool.dtype, device=dev)
+            if tuple(t.shape) != want:
+                raise ValueError(f"{name} must be {want}")
     need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, partition_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", device=dev)
     ws_bytes = workspace.numel() * workspace.element_size()
-    st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
-                         ctypes.byref(desc), block_tables.data_ptr(),
-                         int(block_tables.shape[1]), context_lens.data_ptr(), n,
-                         int(max_context_len), hq, float(scale), out.data_ptr(),
-                         workspace.data_ptr(), ws_bytes, int(partition_tokens),
-                         _stream(stream))
+    tail = (ctypes.byref(desc), block_tables.data_ptr(), int(block_tables.shape[1]),
+            context_lens.data_ptr(), n, int(max_context_len), hq, float(scale),
+            out.data_ptr(), workspace.data_ptr(), ws_bytes, int(partition_tokens),
+            _stream(stream))
+    if new_k is None:
+        st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail)
+        where = "pa_decode"
+    else:
+        st = lib().pa_append_decode(q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(),
+                                    k_pool.data_ptr(), v_pool.data_ptr(), *tail)
+        where = "pa_append_decode"
     if st != PA_OK:
-        raise PaError(st, "pa_decode")
+        raise PaError(st, where)
     return out

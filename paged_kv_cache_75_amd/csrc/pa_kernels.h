@@ -48,6 +48,13 @@ struct DecodeArgs {
   int32_t num_partitions;   // 0 selects the balanced split
   int32_t min_split_tiles;  // balanced split: tiles per workgroup share, at least
   float scale_log2;         // scale * log2(e): scores live in the exp2 domain
+  // Appending decode (nullptr otherwise): token T_i - 1 of sequence i is row i
+  // of new_k / new_v ([num_seqs][num_kv_heads][head_dim]).  The decode reads it
+  // from there, and it is copied to its slot (found through the block table):
+  // by the wave that handles the pair's last tile (balanced split), or by a
+  // copy kernel before the decode (fixed partitions).
+  const void* new_k;
+  const void* new_v;
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);

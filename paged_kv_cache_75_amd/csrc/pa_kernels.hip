@@ -203,6 +203,41 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   }
 }
 
+// Appending decode: copy row (i, h) of new_k / new_v to token T_i - 1 of
+// sequence i, through its block table (lengths clamped as in the decode).
+// Sequences with no tokens and table entries outside the pool are skipped.
+// Work item j (from `first`, step `stride`) moves one 16-byte chunk.
+__device__ void append_rows(const DecodeArgs& a, int row_bytes, int64_t first, int64_t stride) {
+  const int cpr = row_bytes / 16;
+  const int Hkv = a.num_kv_heads;
+  const int64_t per_pool = int64_t(a.num_seqs) * Hkv * cpr;
+  for (int64_t j = first; j < 2 * per_pool; j += stride) {
+    const bool is_v = j >= per_pool;
+    const int64_t jj = is_v ? j - per_pool : j;
+    const int64_t row = jj / cpr;                 // i * Hkv + h
+    const int ch = int(jj - row * cpr);
+    const int i = int(row / Hkv);
+    const int h = int(row - int64_t(i) * Hkv);
+    const int T = min(a.context_lens[i], a.max_context_len);
+    if (T <= 0) continue;
+    const int t = T - 1;
+    const int32_t blk = a.block_tables[int64_t(i) * a.max_blocks_per_seq + (t >> a.log2_block)];
+    if (blk < 0 || blk >= a.num_blocks) continue;
+    const int64_t dst_row =
+        ((int64_t(blk) * Hkv + h) << a.log2_block) | (t & ((1 << a.log2_block) - 1));
+    const uint4* src = reinterpret_cast<const uint4*>(
+        static_cast<const char*>(is_v ? a.new_v : a.new_k) + row * row_bytes);
+    uint4* dst = reinterpret_cast<uint4*>(
+        static_cast<char*>(const_cast<void*>(is_v ? a.v_pool : a.k_pool)) + dst_row * row_bytes);
+    dst[ch] = src[ch];
+  }
+}
+
+__global__ __launch_bounds__(256) void append_kv_kernel(DecodeArgs a, int row_bytes) {
+  append_rows(a, row_bytes, int64_t(blockIdx.x) * blockDim.x + threadIdx.x,
+              int64_t(gridDim.x) * blockDim.x);
+}
+
 // ---------------------------------------------------------------------------
 // decode
 //
@@ -298,14 +333,14 @@ struct MfmaPv {
 
   __device__ static int swz(int t) { return (2 * (t / kRowsPer256)) & (CPR - 1); }
 
-  __device__ void set_lane(int lane) {
+  __device__ __forceinline__ void set_lane(int lane) {
     gq = lane >> 4;
     c = lane & 15;
     rho = lane / CPR;
     chi = lane % CPR;
   }
 
-  __device__ void reset() {
+  __device__ __forceinline__ void reset() {
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     m_run = -INFINITY;
@@ -313,7 +348,7 @@ struct MfmaPv {
   }
 
   // query rows of the pair from global memory ([G][D] contiguous at qrows)
-  __device__ void init(const DecodeArgs& a, int seq, int g, int lane) {
+  __device__ __forceinline__ void init(const DecodeArgs& a, int seq, int g, int lane) {
     set_lane(lane);
     const int head = c < G ? c : G - 1;          // padding columns never dereference
     const uint4* qrow = reinterpret_cast<const uint4*>(
@@ -325,7 +360,7 @@ struct MfmaPv {
   }
 
   // query rows of the pair from an LDS copy ([G][D])
-  __device__ void load_q_lds(const char* qs) {
+  __device__ __forceinline__ void load_q_lds(const char* qs) {
     const int head = c < G ? c : 0;
     const uint4* qrow = reinterpret_cast<const uint4*>(qs + head * kRowBytes);
 #pragma unroll
@@ -336,7 +371,7 @@ struct MfmaPv {
   float alpha_;
 
   // phase 1: the value tile goes to LDS (chunks swizzled per row)
-  __device__ void stage_values(const ValRegs<DT, D>& r, char* vt) {
+  __device__ __forceinline__ void stage_values(const ValRegs<DT, D>& r, char* vt) {
 #pragma unroll
     for (int s = 0; s < VS; ++s) {
       const int row = s * RPI + rho;
@@ -345,7 +380,7 @@ struct MfmaPv {
   }
 
   // phase 2: S^T = K . Q^T, rows >= live masked, online softmax update
-  __device__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
+  __device__ __forceinline__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sc = mfma_chunk<DT>(r.k[kk], qb[kk], sc);
@@ -372,7 +407,7 @@ struct MfmaPv {
   }
 
   // phase 3: O^T = alpha O^T + V^T . P^T
-  __device__ void accumulate(const char* vt) {
+  __device__ __forceinline__ void accumulate(const char* vt) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] *= alpha_;
     const v4i16 pb = pack4<DT>(p_);
@@ -394,7 +429,7 @@ struct MfmaPv {
   // One wave holds the whole segment: write its result from registers.
   // complete: out rows (row0 + c) get O/l; otherwise the piece slot gets
   // O/l, the running max and the sum.  Lane (gq, c < G) owns d = 16n+4gq+i.
-  __device__ void store_result(const DecodeArgs& a, int64_t row0, bool complete, int piece) {
+  __device__ __forceinline__ void store_result(const DecodeArgs& a, int64_t row0, bool complete, int piece) {
     float l = l_run;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
@@ -417,7 +452,7 @@ struct MfmaPv {
 
   // wave totals into sm: O^T lane (gq, c), element i of tile n = head c, d = 16n + 4gq + i
   template <typename Smem>
-  __device__ void finish(Smem& sm, int wave) {
+  __device__ __forceinline__ void finish(Smem& sm, int wave) {
     float l = l_run;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
@@ -763,6 +798,9 @@ constexpr int kPieceFirst = 1;   // the piece starts at the pair's first tile
 constexpr int kPieceLast = 2;    // the piece ends at the pair's last tile
 constexpr int kHdrInts = 8;      // valid, seq, kv head, flags, pieces, (pad)
 constexpr int kQStageBytes = 8192;
+constexpr int kMetaLive = 0x1f;    // tile descriptor: live rows (1..16)
+constexpr int kMetaAppend = 0x20;  // tile descriptor: the last live row is appended
+constexpr int kMetaStore = 0x40;   // ... and its table entry lies in the pool
 
 constexpr int kPairCost = 1;
 
@@ -771,10 +809,12 @@ __device__ inline int pair_units(int T) {
   return tiles ? tiles + kPairCost : 0;
 }
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool kAppend>
 struct StreamSmem {
   static constexpr int kQBytes = G * D * 2;
-  static constexpr int kSegCap = std::max(2, std::min(16, kQStageBytes / kQBytes));
+  // appending decode: each segment's new K and V rows sit beside its queries
+  static constexpr int kNewBytes = kAppend ? 2 * Geo<DT, D, G>::kRowBytes : 0;
+  static constexpr int kSegCap = std::max(2, std::min(16, kQStageBytes / (kQBytes + kNewBytes)));
   alignas(16) char vtile[MfmaPv<DT, D, G>::kScratchBytes];
   alignas(16) char q[kSegCap][kQBytes];
   int32_t len[kMaxSplitSeqs];
@@ -785,12 +825,14 @@ struct StreamSmem {
   int32_t seg_n[kSegCap];
   int32_t seg_flags[kSegCap];
   int32_t seg_pieces[kSegCap];
+  alignas(16) char newkv[kAppend ? kSegCap : 1][kAppend ? kNewBytes : 16];
+  int64_t new_dst[kAppend ? kSegCap : 1];   // pool byte offset of the new row, or -1
 };
 
-template <int DT, int D, int G>
+template <int DT, int D, int G, bool kAppend>
 __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, G>;
-  using SM = StreamSmem<DT, D, G>;
+  using SM = StreamSmem<DT, D, G, kAppend>;
   constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
   constexpr int kRowBytes = GE::kRowBytes;
   __shared__ SM sm;
@@ -827,6 +869,9 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   const long long excl = incl - mine;
   wave_sync_lds();
 
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
+
   // zero-length sequences get zero rows (spread over every workgroup)
   for (int s = w; s < N; s += W)
     if (sm.len[s] == 0) zero_rows<DT, D>(a, int64_t(s) * Hq, Hq);
@@ -851,8 +896,6 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
   const int k_off = c * kRowBytes + gq * 16;          // key chunk gq of row c; +64 per kk
   const int v_off = rho * kRowBytes + chi * 16;       // value chunk chi of row rho
-  const int lb = a.log2_block;
-  const int bmask = (1 << lb) - 1;
   const int64_t blk_rows = int64_t(Hkv) << lb;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
@@ -896,6 +939,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
         sm.seg_n[nseg] = n;
         sm.seg_flags[nseg] = flags | (pos == lo ? 0 : 4);
         sm.seg_pieces[nseg] = int(w_last - w + 1);
+        if constexpr (kAppend) sm.new_dst[nseg] = -1;
       }
       ntot += n;
       ++nseg;
@@ -913,6 +957,17 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
           (int64_t(sm.seg_seq[sg]) * Hq + int64_t(sm.seg_g[sg]) * G) * kRowBytes);
       *reinterpret_cast<uint4*>(sm.q[sg] + part * 16) = src[part];
     }
+    if constexpr (kAppend) {        // new K row, then new V row, of each segment's pair
+      for (int idx = lane; idx < nseg * 2 * CPR; idx += kWave) {
+        const int sg = idx / (2 * CPR);
+        const int part = idx - sg * 2 * CPR;
+        const bool is_v = part >= CPR;
+        const uint4* src = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(is_v ? a.new_v : a.new_k) +
+            (int64_t(sm.seg_seq[sg]) * Hkv + sm.seg_g[sg]) * kRowBytes);
+        *reinterpret_cast<uint4*>(sm.newkv[sg] + part * 16) = src[is_v ? part - CPR : part];
+      }
+    }
 
     // ---- per-tile descriptors, 64 tiles per batch: lane j holds tile
     //      64*batch + j: its first row's byte offset and (segment, live rows)
@@ -927,9 +982,14 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       const int t0 = (sm.seg_tile0[sg] + j - sm.seg_start[sg]) * kTileTokens;
       const int T = sm.len[seq];
       const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
-      const int64_t blk = min(max(table[t0 >> lb], 0), a.num_blocks - 1);
+      const int32_t entry = table[t0 >> lb];
+      const int64_t blk = min(max(entry, 0), a.num_blocks - 1);
       doff = (blk * blk_rows + (int64_t(sm.seg_g[sg]) << lb) + (t0 & bmask)) * kRowBytes;
-      dmeta = min(kTileTokens, T - t0) | (sg << 8);
+      const int live = min(kTileTokens, T - t0);
+      // the sequence's newest token is in this tile and comes from new_k/new_v
+      const bool app = kAppend && t0 + live == T;
+      const bool in_pool = entry == blk;
+      dmeta = live | (app ? kMetaAppend : 0) | (app && in_pool ? kMetaStore : 0) | (sg << 8);
     };
     auto tile_off = [&](int k) -> int64_t {
       const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff), k & 63);
@@ -946,24 +1006,55 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     struct Keys {
       KeyRegs<DT, D> r;
       int meta;
+      int64_t off;                   // byte offset of the tile's first row in the pools
+    };
+    // rows the pool supplies: the live ones, less the newest when it is
+    // appended (that row then reads as zero and never touches the pool)
+    auto pool_rows = [&](int meta) {
+      return (meta & kMetaLive) - ((kAppend && (meta & kMetaAppend)) ? 1 : 0);
     };
     auto load_keys = [&](int k, Keys& kr) {
       if ((k & 63) == 0 && k > 0) load_batch(k >> 6);
       const int meta = tile_meta(k);
-      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, tile_off(k), meta & 0xff);
+      const int64_t off = tile_off(k);
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, off, pool_rows(meta));
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         kr.r.k[kk] = __builtin_bit_cast(
             uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
       kr.meta = meta;
+      kr.off = off;
     };
     ValRegs<DT, D> vr;
     auto load_vals = [&](int k) {
-      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_off(k), tile_meta(k) & 0xff);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_off(k), pool_rows(tile_meta(k)));
 #pragma unroll
       for (int s2 = 0; s2 < VS; ++s2)
         vr.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
                                                  rv, v_off + s2 * RPI * kRowBytes, 0, 0));
+    };
+    // Appending tile: the newest row of the keys and of the values comes from
+    // the segment's LDS copy of new_k / new_v (register selects only, so the
+    // loads in flight are not waited for any earlier than the tile needs).
+    // This wave, the only one to handle that row, also stores it to its pool
+    // slot once the run's tiles are done (a store in the tile pipeline would
+    // hold up the waits for the loads issued after it).  Nothing reads that
+    // slot in this launch: the descriptors of the tile stop short of it.
+    auto put_new_row = [&](Keys& kr) {
+      const int live = kr.meta & kMetaLive;
+      const char* nk = sm.newkv[kr.meta >> 8];
+      if (lane == 0)
+        sm.new_dst[kr.meta >> 8] =
+            (kr.meta & kMetaStore) ? kr.off + int64_t(live - 1) * kRowBytes : int64_t(-1);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const uint4 x = *reinterpret_cast<const uint4*>(nk + (gq + 4 * kk) * 16);
+        if (c == live - 1) kr.r.k[kk] = x;
+      }
+      const uint4 y = *reinterpret_cast<const uint4*>(nk + kRowBytes + chi * 16);
+#pragma unroll
+      for (int s2 = 0; s2 < VS; ++s2)
+        if (rho + s2 * RPI == live - 1) vr.v[s2] = y;
     };
 
     load_batch(0);
@@ -980,9 +1071,11 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
         tm.reset();
         tm.load_q_lds(sm.q[sg]);
       }
+      if constexpr (kAppend)
+        if (kr.meta & kMetaAppend) put_new_row(kr);
       tm.stage_values(vr, sm.vtile);
       if (k + 1 < ntot) load_vals(k + 1);
-      tm.scores(a, kr.r, kr.meta & 0xff);
+      tm.scores(a, kr.r, kr.meta & kMetaLive);
       if (k + 2 < ntot) load_keys(k + 2, kr);
       tm.accumulate(sm.vtile);
       if (k + 1 == sm.seg_start[sg] + sm.seg_n[sg]) {   // the segment's last tile
@@ -1006,6 +1099,18 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       step(k, KA);
       if (k + 1 >= ntot) break;
       step(k + 1, KB);
+    }
+    if constexpr (kAppend) {
+      wave_sync_lds();               // new_dst records of this run
+      for (int sg = 0; sg < nseg; ++sg) {
+        const int64_t dst = sm.new_dst[sg];
+        if (dst >= 0 && lane < 2 * CPR) {
+          const bool is_v = lane >= CPR;
+          char* pool = const_cast<char*>(is_v ? vbase : kbase);
+          *reinterpret_cast<uint4*>(pool + dst + (is_v ? lane - CPR : lane) * 16) =
+              *reinterpret_cast<const uint4*>(sm.newkv[sg] + lane * 16);
+        }
+      }
     }
     wave_sync_lds();                 // LDS records are rewritten by the next run
   }
@@ -1168,20 +1273,38 @@ int resident_workgroups(const void* kernel, int kernel_id, int threads) {
 }
 
 template <int DT, int D, int G>
-hipError_t launch_decode_g(const DecodeArgs& a, hipStream_t stream) {
-  if (a.num_partitions == 0) {
+hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
+  if (args.num_partitions == 0) {
+    const DecodeArgs& a = args;
     // balanced split: 16-bit elements, tiles inside one block (checked by the plan)
     if constexpr (DT == PA_F32) {
       return hipErrorInvalidValue;
     } else {
-      const void* k = reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G>);
-      const int W = resident_workgroups(k, (DT * 1000 + D) * 100 + G, kWave);
+      const bool app = a.new_k != nullptr;
+      const void* k = app ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true>)
+                          : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false>);
+      const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 2 + (app ? 1 : 0), kWave);
       if (W <= 0) return hipErrorInvalidDevice;
-      hipLaunchKernelGGL((decode_stream_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a);
+      if (app)
+        hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, true>), dim3(W), dim3(kWave), 0,
+                           stream, a);
+      else
+        hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, false>), dim3(W), dim3(kWave), 0,
+                           stream, a);
       hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a,
                          W);
     }
   } else {
+    DecodeArgs a = args;
+    if (a.new_k) {
+      // fixed partitions read the pools only: write the new rows first
+      constexpr int kRowBytes = Geo<DT, D, G>::kRowBytes;
+      const int64_t chunks = int64_t(2) * a.num_seqs * a.num_kv_heads * (kRowBytes / 16);
+      const int blocks = int(std::min<int64_t>((chunks + 255) / 256, 4096));
+      hipLaunchKernelGGL(append_kv_kernel, dim3(blocks), dim3(256), 0, stream, a, kRowBytes);
+      a.new_k = nullptr;
+      a.new_v = nullptr;
+    }
     const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
     // a 16-token tile lies inside one block when the block size is a multiple of 16
     if (a.log2_block >= 4) {

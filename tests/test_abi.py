@@ -13,7 +13,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert {"pa_write_kv", "pa_decode", "pa_decode_workspace_bytes", "pa_status_string"} <= set(names)
+    assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_workspace_bytes",
+            "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libpa.so does not export {n}"
@@ -116,3 +117,25 @@ def test_workspace_query():
     rows = 1500 * 32 * 2
     assert B.pa_decode_workspace_bytes(1500, 32, d, 512) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
     assert B.pa_decode_workspace_bytes(256, 31, d, 4096) == 0        # invalid -> 0
+
+
+def append_decode(d, nk=FAKE, nv=FAKE, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=8, cl=FAKE, n=4, maxlen=100, hq=8,
+             scale=0.1, out=FAKE, ws=FAKE, wsb=1 << 20, part=0)
+    a.update(kw)
+    return B.lib().pa_append_decode(a["q"], nk, nv, a["k"], a["v"],
+                                    ctypes.byref(d) if d is not None else None, a["bt"],
+                                    a["mb"], a["cl"], a["n"], a["maxlen"], a["hq"], a["scale"],
+                                    a["out"], a["ws"], a["wsb"], a["part"], None)
+
+
+@pytest.mark.parametrize("nk,nv,kw,want", [
+    (None, FAKE, {}, B.PA_ERR_INVALID_ARGUMENT),         # new rows are required
+    (FAKE, None, {}, B.PA_ERR_INVALID_ARGUMENT),
+    (FAKE, FAKE, dict(hq=7), B.PA_ERR_INVALID_ARGUMENT),  # the decode's own checks
+    (FAKE, FAKE, dict(wsb=1 << 16), B.PA_ERR_WORKSPACE_TOO_SMALL),
+    (FAKE, FAKE, dict(k=None), B.PA_ERR_INVALID_ARGUMENT),
+    (None, None, dict(n=0), B.PA_OK),                     # empty batch: nothing to do
+])
+def test_append_decode_validation(nk, nv, kw, want):
+    assert append_decode(desc(), nk, nv, **kw) == want

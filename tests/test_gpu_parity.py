@@ -278,3 +278,49 @@ def test_workspace_reused_across_calls():
     compare(f64(outs[1]), want_b, "bf16", label="B")
     compare(f64(outs[2]), want_a[:37], "bf16", label="A[:37]")
     assert np.array_equal(_bytes(outs[0]), _bytes(outs[3]))
+
+
+
+# ---------------------------------------------------------------------------
+# pa_append_decode: the decode step in one call
+# ---------------------------------------------------------------------------
+APPEND_CASES = [(3, 1200, 0), (5, 1201, 0), (2, 1202, 0), (3, 1203, 256), (1, 1204, 0)]
+
+
+def _append(dw, partition=0, out=None):
+    from paged_kv_cache_75_amd import pa_append_decode
+    return pa_append_decode(dw.q, dw.new_k, dw.new_v, dw.k_pool, dw.v_pool, dw.block_tables,
+                            dw.context_lens, dw.scale, out=out, max_context_len=dw.max_context_len,
+                            partition_tokens=partition)
+
+
+def _check_append(w, partition, label):
+    fused, split = upload(w, DEV), upload(w, DEV)
+    say(f"[append] {label}: fused call, then write + decode")
+    a = to_host(_append(fused, partition), w.dtype)
+    b = to_host(gpu_step(split, partition_tokens=partition), w.dtype)
+    _sync()
+    assert np.array_equal(_bytes(a), _bytes(b)), "fused and two-call outputs differ"
+    want, k_ref, v_ref = oracle_step(w)
+    compare(ref.to_float64(a, w.dtype), want, w.dtype, label=label)
+    assert np.array_equal(_bytes(to_host(fused.k_pool, w.dtype)), _bytes(k_ref))
+    assert np.array_equal(_bytes(to_host(fused.v_pool, w.dtype)), _bytes(v_ref))
+
+
+@pytest.mark.parametrize("cfg,seed,partition", APPEND_CASES,
+                         ids=[f"cfg{c}-seed{s}-p{p}" for c, s, p in APPEND_CASES])
+def test_append_decode_configs(cfg, seed, partition):
+    """Same output bits as pa_write_kv + pa_decode, the oracle's pools."""
+    _check_append(workloads.make(cfg, seed=seed), partition, f"config {cfg} seed {seed}")
+
+
+@pytest.mark.parametrize("dtype,block_size,group", [("bf16", 16, 4), ("f16", 32, 7),
+                                                    ("f16", 8, 2), ("bf16", 64, 1)])
+def test_append_decode_tile_edges(dtype, block_size, group):
+    """The newest token alone in its tile (T = 1, 17, 33), on the last row of a
+    tile (T = 16, 32), mid-tile, and empty sequences."""
+    lens = [1, 16, 17, 32, 0, 33, 5, 300, 2, 257, 0, 48]
+    hkv = 2
+    w = workloads.random_paged("append-edges", dtype, hkv * group, hkv, 128 if group != 7 else 64,
+                               block_size, lens, seed=1300 + block_size, spare_frac=0.1)
+    _check_append(w, 0, f"{dtype} B={block_size} G={group}")
