@@ -178,6 +178,20 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                            void* out, void* workspace, size_t workspace_bytes,
                            int32_t partition_tokens, void* stream);
 
+/*
+ * pa_profile_start / pa_profile_stop -- kernel timing for measurements; not
+ * needed to compute anything.  Between the two calls, every pa_decode and
+ * pa_append_decode launches its attention kernel (the balanced-split stream
+ * kernel, or the fixed-partition kernel) with a HIP start and stop event
+ * attached to that dispatch; the piece merge is not included.  pa_profile_stop
+ * turns timing off, waits for the recorded events, and returns how many
+ * launches were timed and their mean duration in microseconds (0 launches:
+ * mean 0).  The switch is process-wide; while it is on each call creates two
+ * events, so it does not belong on a path that must not allocate.
+ */
+pa_status pa_profile_start(void);
+pa_status pa_profile_stop(int32_t* launches, double* mean_us);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_string(pa_status status);
 

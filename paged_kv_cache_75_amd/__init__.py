@@ -11,9 +11,11 @@ missing; nothing falls back to another implementation.
 from .binding import (PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED,
                       PA_ERR_WORKSPACE_TOO_SMALL, PA_F16, PA_F32, PA_OK, PaError, lib,
                       pa_append_decode, pa_decode, pa_decode_workspace_bytes, pa_pool_desc,
-                      pa_status_string, pa_write_kv, pool_desc)
+                      pa_profile_start, pa_profile_stop, pa_status_string, pa_write_kv,
+                      pool_desc)
 
 __all__ = ["PA_BF16", "PA_ERR_HIP", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED",
            "PA_ERR_WORKSPACE_TOO_SMALL", "PA_F16", "PA_F32", "PA_OK", "PaError", "lib",
            "pa_append_decode", "pa_decode", "pa_decode_workspace_bytes", "pa_pool_desc",
-           "pa_status_string", "pa_write_kv", "pool_desc"]
+           "pa_profile_start", "pa_profile_stop", "pa_status_string", "pa_write_kv",
+           "pool_desc"]

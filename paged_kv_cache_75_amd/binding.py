@@ -70,6 +70,10 @@ def lib():
     L.pa_append_decode.argtypes = [vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
                                    ctypes.c_float, vp, vp, sz, i32, vp]
     L.pa_append_decode.restype = ctypes.c_int
+    L.pa_profile_start.argtypes = []
+    L.pa_profile_start.restype = ctypes.c_int
+    L.pa_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+    L.pa_profile_stop.restype = ctypes.c_int
     L.pa_status_string.argtypes = [ctypes.c_int]
     L.pa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -78,6 +82,22 @@ def lib():
 
 def pa_status_string(status: int) -> str:
     return lib().pa_status_string(int(status)).decode()
+
+
+def pa_profile_start() -> None:
+    """Time the attention kernel of every decode call until pa_profile_stop."""
+    st = lib().pa_profile_start()
+    if st != PA_OK:
+        raise PaError(st, "pa_profile_start")
+
+
+def pa_profile_stop() -> tuple[int, float]:
+    """Stop timing; (launches timed, their mean duration in microseconds)."""
+    n, mean = ctypes.c_int32(0), ctypes.c_double(0.0)
+    st = lib().pa_profile_stop(ctypes.byref(n), ctypes.byref(mean))
+    if st != PA_OK:
+        raise PaError(st, "pa_profile_stop")
+    return int(n.value), float(mean.value)
 
 
 # ---------------------------------------------------------------------------

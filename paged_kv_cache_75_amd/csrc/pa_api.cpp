@@ -125,6 +125,16 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                 workspace_bytes, partition_tokens, stream);
 }
 
+pa_status pa_profile_start(void) {
+  pa::profile_start();
+  return PA_OK;
+}
+
+pa_status pa_profile_stop(int32_t* launches, double* mean_us) {
+  if (!launches || !mean_us) return PA_ERR_INVALID_ARGUMENT;
+  return pa::profile_stop(launches, mean_us) == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 const char* pa_status_string(pa_status status) {
   switch (status) {
     case PA_OK: return "PA_OK";

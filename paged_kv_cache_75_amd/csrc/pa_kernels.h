@@ -59,6 +59,11 @@ struct DecodeArgs {
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 
+// Kernel timing (measurement only): start attaching events to the attention
+// kernel of each decode call; stop, wait for those events and report.
+void profile_start();
+hipError_t profile_stop(int32_t* launches, double* mean_us);
+
 // dtype is a pa_dtype value; head_dim 64/128; group as planned.
 hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, int32_t head_dim,
                          int32_t group, hipStream_t stream);

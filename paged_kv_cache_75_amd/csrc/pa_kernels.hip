@@ -6,14 +6,17 @@
 // block table[t >> log2B] at offset t & (B-1).  Pools are
 // [num_blocks][num_kv_heads][B][D]: one (block, kv head) pair is B*D
 // contiguous elements, so every row of D elements is read with 16-byte loads.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <map>
 #include <mutex>
 #include <utility>
+#include <vector>
 
 #include "pa_kernels.h"
 
@@ -1272,6 +1275,38 @@ int resident_workgroups(const void* kernel, int kernel_id, int threads) {
   return n;
 }
 
+// ---------------------------------------------------------------------------
+// Kernel timing for measurements (pa_profile_start / pa_profile_stop): while
+// it is on, each call launches its attention kernel with a start and a stop
+// event attached to that dispatch, so the pair brackets the kernel alone.
+struct KernelTimer {
+  std::atomic<bool> on{false};
+  std::mutex mu;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
+};
+KernelTimer& kernel_timer() {
+  static KernelTimer t;
+  return t;
+}
+
+template <typename Kernel, typename... Args>
+void launch_attention(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
+  KernelTimer& t = kernel_timer();
+  if (t.on.load(std::memory_order_relaxed)) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
+      {
+        std::lock_guard<std::mutex> lock(t.mu);
+        t.events.emplace_back(e0, e1);
+      }
+      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
+      return;
+    }
+    if (e0) hipEventDestroy(e0);
+  }
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
+}
+
 template <int DT, int D, int G>
 hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
   if (args.num_partitions == 0) {
@@ -1286,11 +1321,9 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
       const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 2 + (app ? 1 : 0), kWave);
       if (W <= 0) return hipErrorInvalidDevice;
       if (app)
-        hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, true>), dim3(W), dim3(kWave), 0,
-                           stream, a);
+        launch_attention(decode_stream_kernel<DT, D, G, true>, dim3(W), dim3(kWave), stream, a);
       else
-        hipLaunchKernelGGL((decode_stream_kernel<DT, D, G, false>), dim3(W), dim3(kWave), 0,
-                           stream, a);
+        launch_attention(decode_stream_kernel<DT, D, G, false>, dim3(W), dim3(kWave), stream, a);
       hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a,
                          W);
     }
@@ -1308,11 +1341,11 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
     const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
     // a 16-token tile lies inside one block when the block size is a multiple of 16
     if (a.log2_block >= 4) {
-      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, true>), grid,
-                         dim3(kWave * kPartitionWaves), 0, stream, a);
+      launch_attention(decode_partition_kernel<DT, D, G, true>, grid,
+                       dim3(kWave * kPartitionWaves), stream, a);
     } else {
-      hipLaunchKernelGGL((decode_partition_kernel<DT, D, G, false>), grid,
-                         dim3(kWave * kPartitionWaves), 0, stream, a);
+      launch_attention(decode_partition_kernel<DT, D, G, false>, grid,
+                       dim3(kWave * kPartitionWaves), stream, a);
     }
     if (a.num_partitions > 1) {
       const dim3 rgrid(a.num_kv_heads, a.num_seqs);
@@ -1350,6 +1383,36 @@ hipError_t launch_decode_dt(const DecodeArgs& a, int32_t head_dim, int32_t group
 }
 
 }  // namespace
+
+void profile_start() {
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.on.store(true);
+}
+
+hipError_t profile_stop(int32_t* launches, double* mean_us) {
+  KernelTimer& t = kernel_timer();
+  std::lock_guard<std::mutex> lock(t.mu);
+  t.on.store(false);
+  hipError_t err = hipSuccess;
+  double total_ms = 0.0;
+  int32_t n = 0;
+  for (auto& e : t.events) {
+    float ms = 0.0f;
+    if (err == hipSuccess) err = hipEventSynchronize(e.second);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e.first, e.second);
+    if (err == hipSuccess) {
+      total_ms += ms;
+      ++n;
+    }
+    hipEventDestroy(e.first);
+    hipEventDestroy(e.second);
+  }
+  t.events.clear();
+  *launches = n;
+  *mean_us = n ? total_ms * 1e3 / n : 0.0;
+  return err;
+}
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;

@@ -139,3 +139,8 @@ def append_decode(d, nk=FAKE, nv=FAKE, **kw):
 ])
 def test_append_decode_validation(nk, nv, kw, want):
     assert append_decode(desc(), nk, nv, **kw) == want
+
+
+def test_profile_hook_without_launches():
+    B.pa_profile_start()
+    assert B.pa_profile_stop() == (0, 0.0)

@@ -324,3 +324,21 @@ def test_append_decode_tile_edges(dtype, block_size, group):
     w = workloads.random_paged("append-edges", dtype, hkv * group, hkv, 128 if group != 7 else 64,
                                block_size, lens, seed=1300 + block_size, spare_frac=0.1)
     _check_append(w, 0, f"{dtype} B={block_size} G={group}")
+
+
+def test_profile_hook_times_each_attention_kernel():
+    """pa_profile_start/stop time one attention kernel per decode call."""
+    from paged_kv_cache_75_amd import pa_profile_start, pa_profile_stop
+    w = workloads.make(3, seed=1400, num_seqs=32)
+    dw = upload(w, DEV)
+    gpu_step(dw)
+    _sync()
+    pa_profile_start()
+    for part in (0, 0, 128):
+        gpu_step(dw, partition_tokens=part, write=False)
+    _sync()
+    n, mean_us = pa_profile_stop()
+    assert n == 3 and 0.0 < mean_us < 1e5
+    gpu_step(dw, write=False)                 # timing is off again
+    _sync()
+    assert pa_profile_stop() == (0, 0.0)
