@@ -1122,54 +1122,107 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 // Combine the pieces of every pair that starts inside this share: the piece
 // here (slot 0 or 1) and slot 0 of the next pieces-1 shares.  One wave per
 // share; lane t owns float4 quads t, t+64, ... of the pair's [G][D] output.
+// Both headers and, in the same round trip, the two pieces a pair starting
+// here most often has (this share's slot 1, the next share's slot 0) are
+// loaded together; further pieces follow kBatch at a time.  The fold order is
+// fixed by the split alone, so results do not depend on timing.
 template <int DT, int D, int G>
 __global__ __launch_bounds__(kWave) void merge_pieces_kernel(DecodeArgs a, int W) {
   const int w = blockIdx.x;
+  const int lane = threadIdx.x;
   constexpr int kQuads = G * D / 4;
+  constexpr int kQPL = (kQuads + kWave - 1) / kWave;   // quads per lane
+  constexpr int kBatch = 8;
+  int hvalid[2], hseq[2], hg[2], hflags[2], hnp[2];
+#pragma unroll
   for (int slot = 0; slot < 2; ++slot) {
     const int32_t* hdr = a.ws_hdr + (2 * w + slot) * kHdrInts;
-    if (__builtin_amdgcn_readfirstlane(hdr[0]) == 0 ||
-        (__builtin_amdgcn_readfirstlane(hdr[3]) & kPieceFirst) == 0)
-      continue;
-    const int seq = __builtin_amdgcn_readfirstlane(hdr[1]);
-    const int g = __builtin_amdgcn_readfirstlane(hdr[2]);
-    const int np = min(__builtin_amdgcn_readfirstlane(hdr[4]), W - w);
-    const int64_t row0 = int64_t(seq) * a.num_q_heads + int64_t(g) * G;
-    for (int qd = threadIdx.x; qd < kQuads; qd += kWave) {
+    hvalid[slot] = __builtin_amdgcn_readfirstlane(hdr[0]);
+    hseq[slot] = __builtin_amdgcn_readfirstlane(hdr[1]);
+    hg[slot] = __builtin_amdgcn_readfirstlane(hdr[2]);
+    hflags[slot] = __builtin_amdgcn_readfirstlane(hdr[3]);
+    hnp[slot] = __builtin_amdgcn_readfirstlane(hdr[4]);
+  }
+  auto piece_ml = [&](int piece, int h) { return a.ws_ml + (piece * G + h) * 2; };
+  auto piece_o = [&](int piece, int qd) {
+    return reinterpret_cast<const f32x4*>(a.ws_o + int64_t(piece) * G * D)[qd];
+  };
+  // speculative pieces (valid addresses whatever the headers say)
+  const int spec[2] = {2 * w + 1, w + 1 < W ? 2 * (w + 1) : 2 * w};
+  float sm[2][kQPL], sl[2][kQPL];
+  f32x4 so[2][kQPL];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+#pragma unroll
+    for (int j = 0; j < kQPL; ++j) {
+      const int qd = min(lane + kWave * j, kQuads - 1);
+      const float* ml = piece_ml(spec[c], qd / (D / 4));
+      sm[c][j] = ml[0];
+      sl[c][j] = ml[1];
+      so[c][j] = piece_o(spec[c], qd);
+    }
+  }
+#pragma unroll
+  for (int slot = 0; slot < 2; ++slot) {
+    if (hvalid[slot] == 0 || (hflags[slot] & kPieceFirst) == 0) continue;
+    const int np = min(hnp[slot], W - w);
+    const int64_t row0 = int64_t(hseq[slot]) * a.num_q_heads + int64_t(hg[slot]) * G;
+#pragma unroll
+    for (int j = 0; j < kQPL; ++j) {
+      const int qd = lane + kWave * j;
+      if (qd >= kQuads) break;
       const int h = qd / (D / 4);
-      // pieces are read kBatch at a time (all loads in flight together) and
-      // folded into a running (M, L, O) with the usual rescale
-      constexpr int kBatch = 8;
-      float M = -INFINITY, L = 0.0f;
-      f32x4 O = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int p0 = 0; p0 < np; p0 += kBatch) {
+      // pieces 0 and 1 (from the speculative loads where they match)
+      float m0, l0, m1 = -INFINITY, l1 = 0.0f;
+      f32x4 o0, o1 = {0.0f, 0.0f, 0.0f, 0.0f};
+      if (slot == 1) {
+        m0 = sm[0][j];
+        l0 = sl[0][j];
+        o0 = so[0][j];
+      } else {
+        m0 = piece_ml(2 * w, h)[0];
+        l0 = piece_ml(2 * w, h)[1];
+        o0 = piece_o(2 * w, qd);
+      }
+      if (np > 1) {
+        m1 = sm[1][j];
+        l1 = sl[1][j];
+        o1 = so[1][j];
+      }
+      float M = fmaxf(m0, m1);
+      const float w0 = l0 * __builtin_amdgcn_exp2f(m0 - M);
+      const float w1 = np > 1 ? l1 * __builtin_amdgcn_exp2f(m1 - M) : 0.0f;
+      float L = w0 + w1;
+      f32x4 O = w0 * o0 + w1 * o1;
+      // the rest, kBatch at a time (all loads in flight together)
+      for (int p0 = 2; p0 < np; p0 += kBatch) {
         float m[kBatch], l[kBatch];
         f32x4 o[kBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int p = p0 + j;
+        for (int b = 0; b < kBatch; ++b) {
+          const int p = p0 + b;
           if (p < np) {
-            const int piece = p == 0 ? 2 * w + slot : 2 * (w + p);
-            m[j] = a.ws_ml[(piece * G + h) * 2];
-            l[j] = a.ws_ml[(piece * G + h) * 2 + 1];
-            o[j] = reinterpret_cast<const f32x4*>(a.ws_o + int64_t(piece) * G * D)[qd];
+            const float* ml = piece_ml(2 * (w + p), h);
+            m[b] = ml[0];
+            l[b] = ml[1];
+            o[b] = piece_o(2 * (w + p), qd);
           } else {
-            m[j] = -INFINITY;
-            l[j] = 0.0f;
-            o[j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            m[b] = -INFINITY;
+            l[b] = 0.0f;
+            o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
         }
         float Mb = M;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) Mb = fmaxf(Mb, m[j]);
+        for (int b = 0; b < kBatch; ++b) Mb = fmaxf(Mb, m[b]);
         const float f = __builtin_amdgcn_exp2f(M - Mb);
         L *= f;
         O *= f;
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const float wgt = l[j] * __builtin_amdgcn_exp2f(m[j] - Mb);
+        for (int b = 0; b < kBatch; ++b) {
+          const float wgt = l[b] * __builtin_amdgcn_exp2f(m[b] - Mb);
           L += wgt;
-          O += wgt * o[j];
+          O += wgt * o[b];
         }
         M = Mb;
       }
