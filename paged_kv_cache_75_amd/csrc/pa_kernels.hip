@@ -1120,18 +1120,28 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 }
 
 // Combine the pieces of every pair that starts inside this share: the piece
-// here (slot 0 or 1) and slot 0 of the next pieces-1 shares.  One wave per
-// share; lane t owns float4 quads t, t+64, ... of the pair's [G][D] output.
-// Both headers and, in the same round trip, the two pieces a pair starting
-// here most often has (this share's slot 1, the next share's slot 0) are
-// loaded together; further pieces follow kBatch at a time.  The fold order is
-// fixed by the split alone, so results do not depend on timing.
+// here (slot 0 or 1) and slot 0 of the next pieces-1 shares.  One workgroup
+// per share, one thread per float4 quad of the pair's [G][D] output (so that
+// every load of a batch is in flight at once).  Both headers and, in the same
+// round trip, the two pieces a pair starting here most often has (this
+// share's slot 1, the next share's slot 0) are loaded together; further
+// pieces follow kBatch at a time.  The fold order is fixed by the split alone,
+// so results do not depend on timing.
+template <int G, int D>
+struct MergeShape {
+  static constexpr int kQuads = G * D / 4;
+  static constexpr int kThreads = std::min(256, (kQuads + kWave - 1) / kWave * kWave);
+  static constexpr int kQPT = (kQuads + kThreads - 1) / kThreads;   // quads per thread
+};
+
 template <int DT, int D, int G>
-__global__ __launch_bounds__(kWave) void merge_pieces_kernel(DecodeArgs a, int W) {
+__global__ __launch_bounds__((MergeShape<G, D>::kThreads)) void merge_pieces_kernel(DecodeArgs a,
+                                                                                    int W) {
+  using MS = MergeShape<G, D>;
   const int w = blockIdx.x;
-  const int lane = threadIdx.x;
-  constexpr int kQuads = G * D / 4;
-  constexpr int kQPL = (kQuads + kWave - 1) / kWave;   // quads per lane
+  const int tid = threadIdx.x;
+  constexpr int kQuads = MS::kQuads;
+  constexpr int kQPT = MS::kQPT;
   constexpr int kBatch = 8;
   int hvalid[2], hseq[2], hg[2], hflags[2], hnp[2];
 #pragma unroll
@@ -1149,13 +1159,13 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(DecodeArgs a, int W
   };
   // speculative pieces (valid addresses whatever the headers say)
   const int spec[2] = {2 * w + 1, w + 1 < W ? 2 * (w + 1) : 2 * w};
-  float sm[2][kQPL], sl[2][kQPL];
-  f32x4 so[2][kQPL];
+  float sm[2][kQPT], sl[2][kQPT];
+  f32x4 so[2][kQPT];
 #pragma unroll
   for (int c = 0; c < 2; ++c) {
 #pragma unroll
-    for (int j = 0; j < kQPL; ++j) {
-      const int qd = min(lane + kWave * j, kQuads - 1);
+    for (int j = 0; j < kQPT; ++j) {
+      const int qd = min(tid + MS::kThreads * j, kQuads - 1);
       const float* ml = piece_ml(spec[c], qd / (D / 4));
       sm[c][j] = ml[0];
       sl[c][j] = ml[1];
@@ -1168,8 +1178,8 @@ __global__ __launch_bounds__(kWave) void merge_pieces_kernel(DecodeArgs a, int W
     const int np = min(hnp[slot], W - w);
     const int64_t row0 = int64_t(hseq[slot]) * a.num_q_heads + int64_t(hg[slot]) * G;
 #pragma unroll
-    for (int j = 0; j < kQPL; ++j) {
-      const int qd = lane + kWave * j;
+    for (int j = 0; j < kQPT; ++j) {
+      const int qd = tid + MS::kThreads * j;
       if (qd >= kQuads) break;
       const int h = qd / (D / 4);
       // pieces 0 and 1 (from the speculative loads where they match)
@@ -1355,7 +1365,7 @@ void launch_attention(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, 
       hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
       return;
     }
-    if (e0) hipEventDestroy(e0);
+    if (e0) (void)hipEventDestroy(e0);
   }
   hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
 }
@@ -1377,8 +1387,8 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
         launch_attention(decode_stream_kernel<DT, D, G, true>, dim3(W), dim3(kWave), stream, a);
       else
         launch_attention(decode_stream_kernel<DT, D, G, false>, dim3(W), dim3(kWave), stream, a);
-      hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W), dim3(kWave), 0, stream, a,
-                         W);
+      hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W),
+                         dim3(MergeShape<G, D>::kThreads), 0, stream, a, W);
     }
   } else {
     DecodeArgs a = args;
@@ -1458,8 +1468,8 @@ hipError_t profile_stop(int32_t* launches, double* mean_us) {
       total_ms += ms;
       ++n;
     }
-    hipEventDestroy(e.first);
-    hipEventDestroy(e.second);
+    (void)hipEventDestroy(e.first);
+    (void)hipEventDestroy(e.second);
   }
   t.events.clear();
   *launches = n;
