@@ -19,6 +19,11 @@ the pages:
 * Same page, section "How is vLLM's KV cache paged?": a new token's K and V
   are copied into slot ``block_table[floor(t / B)] * B + (t mod B)``; the list
   of these per-token slots is the slot mapping.
+* Same page, section "How does it support prompts of arbitrary length? Does it
+  have a sliding window?": in a layer trained with a sliding window of ``W``
+  tokens each token attends only to the last ``W`` tokens, so only the blocks
+  inside the window are needed (at most ``ceil(W / B) + 1`` of them) and older
+  ones may already be released.
 
 Readings taken where the pages leave a step open:
 
@@ -35,6 +40,9 @@ Readings taken where the pages leave a step open:
 * The softmax subtracts the row maximum first, an exact identity.
 * A negative slot in the slot mapping means "no token"; slots must be
   distinct.
+* Sliding window: the token being decoded (position ``T - 1``) is one of the
+  last ``W`` tokens, so the keys are positions ``max(0, T - W) .. T - 1``; table
+  entries of blocks wholly before them are never read.
 
 Parity pins (tests/test_oracle_pins.py): contiguous brute force, a torch
 float64 rendering of the page's sketch, placement invariance, shared-prefix
@@ -169,6 +177,37 @@ def gather_tokens(pool: np.ndarray, table_row, num_tokens: int,
     return to_float64(pool[p, :, r, :], dtype)
 
 
+def window_start(num_tokens: int, window) -> int:
+    """First position a decoded token attends to: the last ``window`` tokens,
+    the newest included (``None``: every token)."""
+    if window is None:
+        return 0
+    return max(0, int(num_tokens) - int(window))
+
+
+def gather_window(pool: np.ndarray, table_row, first: int, num_tokens: int,
+                  block_size: int, dtype: str) -> np.ndarray:
+    """float64 [T - first][Hkv][D]: rows of tokens first .. T-1 in token order.
+    Only table entries of blocks holding those tokens are read."""
+    num_blocks = pool.shape[0]
+    if blocks_for_tokens(num_tokens, block_size) > len(table_row):
+        raise ValueError("context longer than the block table")
+    t = np.arange(first, num_tokens, dtype=np.int64)
+    p, r = token_location(table_row, t, block_size)
+    if t.size and (p.min() < 0 or p.max() >= num_blocks):
+        raise ValueError("block table entry outside the pool")
+    return to_float64(pool[p, :, r, :], dtype)
+
+
+def window_blocks(num_tokens: int, window, block_size: int) -> int:
+    """Blocks a sequence of T tokens needs under a sliding window: those that
+    hold positions window_start(T) .. T-1."""
+    if num_tokens <= 0:
+        return 0
+    first = window_start(num_tokens, window)
+    return (num_tokens - 1) // block_size - first // block_size + 1
+
+
 def attend(q_h: np.ndarray, keys: np.ndarray, values: np.ndarray,
            scale: float) -> np.ndarray:
     """softmax(scale * keys . q_h) . values for one query row, in float64.
@@ -182,13 +221,14 @@ def attend(q_h: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
            block_tables: np.ndarray, context_lens, scale: float,
-           dtype: str, seqs=None) -> np.ndarray:
+           dtype: str, seqs=None, window=None) -> np.ndarray:
     """Decode-step attention for every (sequence, query head); float64 out.
 
     q: [N][Hq][D]; pools: [num_blocks][Hkv][B][D]; block_tables: int [N][MB];
     context_lens: int [N] (T_i counts the newest token, whose K/V is already in
     the pool).  ``seqs`` restricts the work to some sequences (their rows of the
     result are filled, the others are left NaN) for sampled checks at full size.
+    ``window``: a sliding window of that many tokens (None: full attention).
     """
     num_seqs, num_q_heads, head_dim = q.shape
     _, num_kv_heads, block_size, pool_dim = k_pool.shape
@@ -205,8 +245,13 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         if T == 0:
             out[i] = 0.0
             continue
-        keys = gather_tokens(k_pool, block_tables[i], T, block_size, dtype)
-        values = gather_tokens(v_pool, block_tables[i], T, block_size, dtype)
+        if window is None:
+            keys = gather_tokens(k_pool, block_tables[i], T, block_size, dtype)
+            values = gather_tokens(v_pool, block_tables[i], T, block_size, dtype)
+        else:
+            first = window_start(T, window)
+            keys = gather_window(k_pool, block_tables[i], first, T, block_size, dtype)
+            values = gather_window(v_pool, block_tables[i], first, T, block_size, dtype)
         for h in range(num_q_heads):
             g = kv_head_for_query_head(h, num_q_heads, num_kv_heads)
             out[i, h] = attend(q64[i, h], keys[:, g, :], values[:, g, :], sc)

@@ -351,6 +351,89 @@ def pin_poison_isolated(o):
     assert np.isnan(before).all(axis=(1, 2)).all()
 
 
+# ---------------------------------------------------------------------------
+# sliding window ("vLLM Framework and Inference Engine Design", section "How
+# does it support prompts of arbitrary length? Does it have a sliding window?")
+# ---------------------------------------------------------------------------
+def _release_before_window(bt, lens, window, B, k_pool, v_pool):
+    """Blocks wholly before each sequence's window may be released: their
+    table entries become -1 and their contents NaN (private blocks here)."""
+    bt, kp, vp = bt.copy(), k_pool.copy(), v_pool.copy()
+    for i, T in enumerate(lens):
+        for j in range(max(0, int(T) - window) // B):
+            kp[bt[i, j]] = np.nan
+            vp[bt[i, j]] = np.nan
+            bt[i, j] = -1
+    return bt, kp, vp
+
+
+WINDOW_CASES = [
+    dict(seed=31, lens=[1, 5, 11, 16, 17, 40], Hq=4, Hkv=2, D=8, B=4),
+    dict(seed=32, lens=[3, 33, 2, 0], Hq=6, Hkv=3, D=6, B=2),
+    dict(seed=33, lens=[37, 64], Hq=8, Hkv=1, D=4, B=8),
+]
+
+
+def pin_window_bruteforce(o):
+    """Each query attends to exactly the last W tokens: the contiguous brute
+    force over those tokens, with the blocks before the window released."""
+    for c in WINDOW_CASES:
+        q, kp, vp, bt, lens, ck, cv = _tiny_problem(c["seed"], c["lens"], c["Hq"], c["Hkv"],
+                                                    c["D"], c["B"])
+        scale = float(np.float32(0.41))
+        G = c["Hq"] // c["Hkv"]
+        for W in (1, 2, 3, 5, 16, 21):
+            bt_r, kp_r, vp_r = _release_before_window(bt, lens, W, c["B"], kp, vp)
+            got = o.decode(q, kp_r, vp_r, bt_r, lens, scale, "f32", window=W)
+            for i, T in enumerate(lens):
+                first = max(0, int(T) - W)
+                want = np.array(_brute(q[i].tolist(), ck[i][first:].tolist(),
+                                       cv[i][first:].tolist(), scale, G))
+                np.testing.assert_allclose(got[i], want, rtol=1e-12, atol=1e-13)
+
+
+def pin_window_closed_forms(o):
+    """W >= T is full attention (the same numbers, bit for bit); W = 1 returns
+    the newest token's value row exactly; T = 0 stays zero."""
+    c = WINDOW_CASES[0]
+    q, kp, vp, bt, lens, ck, cv = _tiny_problem(c["seed"], c["lens"], c["Hq"], c["Hkv"],
+                                                c["D"], c["B"])
+    full = o.decode(q, kp, vp, bt, lens, 0.3, "f32")
+    for W in (int(max(lens)), 10 ** 9):
+        assert np.array_equal(o.decode(q, kp, vp, bt, lens, 0.3, "f32", window=W), full)
+    one = o.decode(q, kp, vp, bt, lens, 0.3, "f32", window=1)
+    G = c["Hq"] // c["Hkv"]
+    for i, T in enumerate(lens):
+        for h in range(c["Hq"]):
+            want = cv[i][T - 1][h // G] if T else np.zeros(c["D"])
+            assert np.array_equal(one[i, h], np.asarray(want, dtype=np.float64))
+    z = o.decode(q[:1], kp, vp, bt[:1], np.array([0]), 0.3, "f32", window=4)
+    assert np.array_equal(z, np.zeros_like(z))
+
+
+def pin_window_blocks(o):
+    """Blocks a windowed sequence needs: exactly the distinct blocks of its
+    last W positions; at most ceil((W-1)/B) + 1 over all lengths, which is
+    within the page's bound ceil(W/B) + 1 and equals it unless B divides
+    W - 1, as in the page's Mistral example (W = 4,096, B = 16: at most 257)."""
+    s = load_golden()["sliding_window"]
+    worst = max(o.window_blocks(T, s["window"], s["block_size"])
+                for T in range(1, 3 * s["window"]))
+    assert worst == s["max_blocks"]
+    for B in (1, 4, 16):
+        for W in (1, 5, 16, 17, 64):
+            bound = -(-W // B) + 1
+            seen = 0
+            for T in range(0, 3 * W + 2 * B):
+                first = o.window_start(T, W)
+                distinct = len({t // B for t in range(first, T)})
+                n = o.window_blocks(T, W, B)
+                assert n == distinct and n <= bound
+                seen = max(seen, n)
+            assert seen == -(-(W - 1) // B) + 1
+            assert (seen == bound) == ((W - 1) % B != 0)
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce,
     pin_page_sketch_torch,
@@ -365,4 +448,7 @@ ALL_PINS = [
     pin_byte_accounting,
     pin_toy_batch_config,
     pin_poison_isolated,
+    pin_window_bruteforce,
+    pin_window_closed_forms,
+    pin_window_blocks,
 ]

@@ -85,6 +85,16 @@ def _write_kv_swapped(k_pool, v_pool, k, v, slot_mapping, block_size):
 
 
 MUTANTS["write_swaps_k_v"] = ("write_kv", _write_kv_swapped)
+MUTANTS["window_one_extra"] = ("window_start", lambda T, W: 0 if W is None else max(0, int(T) - int(W) - 1))
+MUTANTS["window_one_short"] = ("window_start", lambda T, W: 0 if W is None else max(0, int(T) - int(W) + 1))
+MUTANTS["window_counts_from_start"] = ("window_start", lambda T, W: 0)
+
+
+def _gather_window_all(pool, table_row, first, num_tokens, block_size, dtype):
+    return ref.__dict__["_orig_gather"](pool, table_row, num_tokens, block_size, dtype)
+
+
+MUTANTS["window_ignored_in_gather"] = ("gather_window", _gather_window_all)
 
 
 def _run_pins():
