@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--step", choices=("both", "append", "two-call"), default="both",
                     help="where the batch writes new tokens: time pa_append_decode (headline) "
                          "and pa_write_kv + pa_decode (both), or only one of them")
+    ap.add_argument("--window", type=int, default=0,
+                    help="sliding window in tokens (pa_decode_sliding; 0 = full attention)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -74,7 +76,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, window: int = 0):
     """The oracle as it stands (write, then decode), on the same host arrays,
     one BLAS thread; repeated over growing sequence samples until the budget
     is spent.  Returns TB/s of KV bytes read, the sample description, cores."""
@@ -89,9 +91,9 @@ def cpu_baseline(w, budget_s: float):
             t0 = time.perf_counter()
             k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size)
             ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
-                       seqs=np.arange(n))
+                       seqs=np.arange(n), window=window or None)
             secs += time.perf_counter() - t0
-            bytes_done += kv_bytes_per_step(w)
+            bytes_done += kv_bytes_per_step(w, window)
             reps += 1
     sample = f"{reps} full steps of the same batch (write + decode, all {n} seqs), {secs:.1f} s"
     return bytes_done / secs / 1e12, sample, 1
@@ -117,10 +119,15 @@ def profiled_traffic(cfg):
     return prof["traffic_bytes_per_launch"], prof
 
 
-def kv_bytes_per_step(w) -> int:
-    """Algorithmic KV bytes of one decode step: every cached token's K and V
-    row, once per kv head."""
-    return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(w.context_lens.astype("int64").sum())
+def kv_bytes_per_step(w, window: int = 0) -> int:
+    """Algorithmic KV bytes of one decode step: every attended token's K and V
+    row, once per kv head (with a sliding window, the last `window` tokens of
+    each sequence)."""
+    import numpy as np
+    lens = w.context_lens.astype("int64")
+    if window:
+        lens = np.minimum(lens, window)
+    return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(lens.sum())
 
 
 def main():
@@ -137,8 +144,9 @@ def main():
     import torch
 
     import workloads
-    from paged_kv_cache_75_amd import (pa_append_decode, pa_decode, pa_decode_workspace_bytes,
-                                       pa_profile_start, pa_profile_stop, pa_write_kv, pool_desc)
+    from paged_kv_cache_75_amd import (pa_append_decode, pa_decode, pa_decode_sliding,
+                                       pa_decode_workspace_bytes, pa_profile_start,
+                                       pa_profile_stop, pa_write_kv, pool_desc)
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -171,8 +179,13 @@ def main():
     writes = cfg in (3, 5)
 
     def decode(kp, vp):
-        pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
-                  workspace=ws, partition_tokens=args.partition)
+        if args.window:
+            pa_decode_sliding(q, kp, vp, bt, cl, w.scale, args.window, out=out,
+                              max_context_len=w.max_context_len, workspace=ws,
+                              partition_tokens=args.partition)
+        else:
+            pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
+                      workspace=ws, partition_tokens=args.partition)
 
     def append_decode(kp, vp):
         pa_append_decode(q, nk, nv, kp, vp, bt, cl, w.scale, out=out,
@@ -225,7 +238,7 @@ def main():
         pass
 
     K = args.steps
-    fused = writes and args.step != "two-call"
+    fused = writes and args.step != "two-call" and not args.window
     two_call = writes and args.step != "append"
     if two_call:
         two_ms, two_decode_ms, two_kernel_us = timed(write, decode)
@@ -236,14 +249,14 @@ def main():
     else:
         ms_per_step, decode_ms, kernel_us = timed(nothing, decode)
 
-    kv_bytes = kv_bytes_per_step(w)
+    kv_bytes = kv_bytes_per_step(w, args.window)
     balanced = args.partition == 0 and w.dtype != "f32" and w.block_size >= 16 and w.num_seqs <= 1024
     attention_kernel = "decode_stream_kernel" if balanced else "decode_partition_kernel"
     decode_ms_mean = sum(decode_ms) / len(decode_ms)
     achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
 
-    traffic_bytes, prof = profiled_traffic(cfg)
+    traffic_bytes, prof = profiled_traffic(cfg) if not args.window and fused else (None, None)
     traffic = None if traffic_bytes is None else round(traffic_bytes)
     result = {
         "metric": "paged decode attention: KV bytes read/s (TB/s), % HBM peak, us/step",
@@ -261,7 +274,7 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[cfg],
+            "workload": WORKLOAD_NAMES[cfg] + (f", sliding window {args.window}" if args.window else ""),
             "seed": seed,
             "num_seqs": w.num_seqs,
             "sum_context_tokens": int(w.context_lens.sum()),
@@ -271,12 +284,14 @@ def main():
             "pool_copies_rotated": reps,
             "partition_tokens": args.partition or "auto",
             "step_calls": ("pa_append_decode" if fused else
-                           "pa_write_kv + pa_decode" if writes else "pa_decode"),
+                           ("pa_write_kv + " if writes else "") +
+                           ("pa_decode_sliding" if args.window else "pa_decode")),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": (attention_kernel + " (attention kernel of " +
-                       ("pa_append_decode" if fused else "pa_decode") + ")"),
+                       ("pa_append_decode" if fused else
+                        "pa_decode_sliding" if args.window else "pa_decode") + ")"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
@@ -300,7 +315,7 @@ def main():
             "kernel_us_mean": round(two_kernel_us, 2),
         }
     if not args.no_cpu_baseline:
-        v, sample, cores = cpu_baseline(w, args.cpu_seconds)
+        v, sample, cores = cpu_baseline(w, args.cpu_seconds, args.window)
         result["cpu_baseline"] = {"value": round(v, 6), "unit": "TB/s", "cores": cores,
                                   "kind": "oracle", "sample": sample}
     print(json.dumps(result), flush=True)

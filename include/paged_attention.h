@@ -147,6 +147,30 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t partition_tokens, void* stream);
 
 /*
+ * pa_decode_sliding -- pa_decode for a layer trained with sliding-window
+ * attention ("vLLM Framework and Inference Engine Design", section "How does
+ * it support prompts of arbitrary length? Does it have a sliding window?":
+ * each token attends only to the last W tokens, so only the blocks inside the
+ * window are needed and older ones may be released).
+ *
+ *   window        W >= 1 tokens: the token being decoded (position T_i - 1)
+ *                 attends to positions max(0, T_i - W) .. T_i - 1.  W >= T_i
+ *                 gives pa_decode's result bit for bit.
+ *   block_tables  only entries of blocks holding those positions are read
+ *                 (at most ceil(W / B) + 1 per sequence); entries before them
+ *                 may hold anything, e.g. -1 for released blocks.
+ *
+ * Every other argument, the workspace query and the error behaviour are those
+ * of pa_decode.  window < 1 returns PA_ERR_INVALID_ARGUMENT.
+ */
+pa_status pa_decode_sliding(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, int32_t window, void* out, void* workspace,
+                            size_t workspace_bytes, int32_t partition_tokens, void* stream);
+
+/*
  * pa_append_decode -- one whole decode step in one call: every sequence's
  * newest token is placed in the pools and then attended over, with the same
  * result as

@@ -60,22 +60,28 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     desc = ctypes.POINTER(pa_pool_desc)
-    L.pa_write_kv.argtypes = [vp, vp, vp, i32, vp, vp, desc, vp]
-    L.pa_write_kv.restype = ctypes.c_int
-    L.pa_decode_workspace_bytes.argtypes = [i32, i32, desc, i32, i32]
-    L.pa_decode_workspace_bytes.restype = sz
-    L.pa_decode.argtypes = [vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
-                            vp, vp, sz, i32, vp]
-    L.pa_decode.restype = ctypes.c_int
-    L.pa_append_decode.argtypes = [vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
-                                   ctypes.c_float, vp, vp, sz, i32, vp]
-    L.pa_append_decode.restype = ctypes.c_int
-    L.pa_profile_start.argtypes = []
-    L.pa_profile_start.restype = ctypes.c_int
-    L.pa_profile_stop.argtypes = [ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
-    L.pa_profile_stop.restype = ctypes.c_int
-    L.pa_status_string.argtypes = [ctypes.c_int]
-    L.pa_status_string.restype = ctypes.c_char_p
+    c_int = ctypes.c_int
+    signatures = {
+        "pa_write_kv": ([vp, vp, vp, i32, vp, vp, desc, vp], c_int),
+        "pa_decode_workspace_bytes": ([i32, i32, desc, i32, i32], sz),
+        "pa_decode": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                       vp, vp, sz, i32, vp], c_int),
+        "pa_decode_sliding": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                               i32, vp, vp, sz, i32, vp], c_int),
+        "pa_append_decode": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
+                              ctypes.c_float, vp, vp, sz, i32, vp], c_int),
+        "pa_profile_start": ([], c_int),
+        "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
+                            c_int),
+        "pa_status_string": ([c_int], ctypes.c_char_p),
+    }
+    # a symbol the library lacks stays undeclared: calling it raises
+    # AttributeError (tests/test_abi.py checks that every one is exported)
+    for name, (args, res) in signatures.items():
+        if hasattr(L, name):
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
     _lib = L
     return L
 
@@ -182,6 +188,15 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
                    max_context_len, workspace, partition_tokens, stream)
 
 
+def pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, window: int,
+                      out=None, max_context_len=None, workspace=None, partition_tokens: int = 0,
+                      stream=None):
+    """pa_decode over each sequence's last ``window`` tokens only (a layer
+    trained with sliding-window attention)."""
+    return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
+                   max_context_len, workspace, partition_tokens, stream, window=int(window))
+
+
 def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,
                      out=None, max_context_len=None, workspace=None,
                      partition_tokens: int = 0, stream=None):
@@ -193,7 +208,7 @@ def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens
 
 
 def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, out,
-            max_context_len, workspace, partition_tokens, stream):
+            max_context_len, workspace, partition_tokens, stream, window=None):
     torch = _torch()
     desc = pool_desc(k_pool)
     dev = k_pool.device
@@ -231,7 +246,11 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
             context_lens.data_ptr(), n, int(max_context_len), hq, float(scale),
             out.data_ptr(), workspace.data_ptr(), ws_bytes, int(partition_tokens),
             _stream(stream))
-    if new_k is None:
+    if window is not None:
+        st = lib().pa_decode_sliding(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                     *tail[:8], int(window), *tail[8:])
+        where = "pa_decode_sliding"
+    elif new_k is None:
         st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail)
         where = "pa_decode"
     else:

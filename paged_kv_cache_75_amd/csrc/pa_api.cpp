@@ -52,7 +52,7 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                  int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
                  void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                 void* stream) {
+                 int32_t window, void* stream) {
   pa::DecodePlan plan;
   pa_status s = pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len,
                                 max_blocks_per_seq, partition_tokens, &plan);
@@ -92,6 +92,7 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
   a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
   a.new_k = new_k;
   a.new_v = new_v;
+  a.window = window;
   const hipError_t e = pa::launch_decode(a, pool->dtype, pool->head_dim, plan.group,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
@@ -109,7 +110,19 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t partition_tokens, void* stream) {
   return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                 context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
-                workspace_bytes, partition_tokens, stream);
+                workspace_bytes, partition_tokens, 0, stream);
+}
+
+pa_status pa_decode_sliding(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, int32_t window, void* out, void* workspace,
+                            size_t workspace_bytes, int32_t partition_tokens, void* stream) {
+  if (window < 1) return PA_ERR_INVALID_ARGUMENT;
+  return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                workspace_bytes, partition_tokens, window, stream);
 }
 
 pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
@@ -122,7 +135,7 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
   if (num_seqs > 0 && (!new_k || !new_v)) return PA_ERR_INVALID_ARGUMENT;
   return decode(q, new_k, new_v, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                 context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
-                workspace_bytes, partition_tokens, stream);
+                workspace_bytes, partition_tokens, 0, stream);
 }
 
 pa_status pa_profile_start(void) {

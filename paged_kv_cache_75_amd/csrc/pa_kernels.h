@@ -55,6 +55,7 @@ struct DecodeArgs {
   // copy kernel before the decode (fixed partitions).
   const void* new_k;
   const void* new_v;
+  int32_t window;           // sliding window in tokens; 0: attend to every token
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);

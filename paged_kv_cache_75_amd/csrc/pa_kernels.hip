@@ -280,6 +280,28 @@ struct ValRegs {
   uint4 v[Geo<DT, D, 1>::VS];
 };
 
+// Sliding window ("vLLM Framework and Inference Engine Design", section on
+// sliding windows): a decoded token attends to the last `window` tokens, the
+// newest included; window 0 attends to every token.  First position, and the
+// 16-token tiles from the one holding it to the end of the sequence.
+__device__ inline int window_first(int T, int window) {
+  return window > 0 ? max(0, T - window) : 0;
+}
+__device__ inline int attended_tiles(int T, int window) {
+  return T > 0 ? (T + kTileTokens - 1) / kTileTokens - window_first(T, window) / kTileTokens : 0;
+}
+
+// Value rows before the window's first position (in the tile holding it) are
+// zeroed: their weight is zero, and zero times a non-finite stale value would
+// not be.  Lane (rho, chi) holds rows rho, rho + RPI, ...
+template <int DT, int D>
+__device__ inline void clear_rows_below(ValRegs<DT, D>& v, int first, int rho) {
+  constexpr int RPI = Geo<DT, D, 1>::RPI, VS = Geo<DT, D, 1>::VS;
+#pragma unroll
+  for (int s = 0; s < VS; ++s)
+    if (rho + s * RPI < first) v.v[s] = make_uint4(0, 0, 0, 0);
+}
+
 // ---------------------------------------------------------------------------
 // Tile math for 16-bit elements: both products on the matrix cores.
 //   Scores transposed, S^T = K . Q^T: A = the key tile (row = token c, as
@@ -383,7 +405,9 @@ struct MfmaPv {
   }
 
   // phase 2: S^T = K . Q^T, rows >= live masked, online softmax update
-  __device__ __forceinline__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
+  // rows first .. live-1 of the tile take part; the others get weight zero
+  __device__ __forceinline__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int first,
+                                         int live) {
     f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) sc = mfma_chunk<DT>(r.k[kk], qb[kk], sc);
@@ -391,7 +415,8 @@ struct MfmaPv {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[i] = 4 * gq + i < live ? sc[i] * a.scale_log2 : -INFINITY;
+      const int row = 4 * gq + i;
+      s[i] = row >= first && row < live ? sc[i] * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
@@ -524,8 +549,8 @@ struct ValuPv {
 
   __device__ void stage_values(const ValRegs<DT, D>& r, char*) { vals_ = r; }
 
-  __device__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int live) {
-    const bool valid = c < live;
+  __device__ void scores(const DecodeArgs& a, const KeyRegs<DT, D>& r, int first, int live) {
+    const bool valid = c >= first && c < live;
     float alpha[NHB][4];
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -632,12 +657,13 @@ struct SegmentSmem {
 // sm.m / sm.l / sm.o hold every wave's max, sum and unnormalised output.
 template <int DT, int D, int G, bool kTileInBlock, int NW>
 __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G, NW>& sm, int seq, int g,
-                               int T, int tile_lo, int tile_hi) {
+                               int T, int s0, int tile_lo, int tile_hi) {
   // the segment is the same for every lane; say so, so that addresses and
   // buffer descriptors derived from it stay in scalar registers
   seq = __builtin_amdgcn_readfirstlane(seq);
   g = __builtin_amdgcn_readfirstlane(g);
   T = __builtin_amdgcn_readfirstlane(T);
+  s0 = __builtin_amdgcn_readfirstlane(s0);
   tile_lo = __builtin_amdgcn_readfirstlane(tile_lo);
   tile_hi = __builtin_amdgcn_readfirstlane(tile_hi);
   using GE = Geo<DT, D, G>;
@@ -690,9 +716,11 @@ __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G, NW>& s
                                              min(kTileTokens, T - t0) * kRowBytes, kBufferDword3);
   };
   // Without that (blocks smaller than a tile) each lane finds its own block;
-  // tokens past T-1 read row T-1 (finite data of this sequence, weight zero).
+  // tokens past T-1 read row T-1 and tokens before the window's first
+  // position s0 read row s0 (data of this sequence, weight zero), so no table
+  // entry outside the attended positions is read.
   auto row_of = [&](int t0, int dt) -> int64_t {
-    const int t = t0 + min(dt, T - 1 - t0);
+    const int t = max(s0, t0 + min(dt, T - 1 - t0));
     const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
     return blk * blk_rows + head_rows + (t & bmask);
   };
@@ -735,9 +763,12 @@ __device__ void attend_segment(const DecodeArgs& a, SegmentSmem<DT, D, G, NW>& s
     load_values(0, VR);
     if (nmine > 1) load_keys(1, KB);
     auto step = [&](int k, KeyRegs<DT, D>& kr) {
+      const int t0 = tile_start(k);
+      const int first = max(0, s0 - t0);
+      if (first > 0) clear_rows_below(VR, first, rho);
       tm.stage_values(VR, scratch);
       if (k + 1 < nmine) load_values(k + 1, VR);
-      tm.scores(a, kr, min(kTileTokens, T - tile_start(k)));
+      tm.scores(a, kr, first, min(kTileTokens, T - t0));
       if (k + 2 < nmine) {
         if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
         load_keys(k + 2, kr);
@@ -807,8 +838,8 @@ constexpr int kMetaStore = 0x40;   // ... and its table entry lies in the pool
 
 constexpr int kPairCost = 1;
 
-__device__ inline int pair_units(int T) {
-  const int tiles = (T + kTileTokens - 1) / kTileTokens;
+__device__ inline int pair_units(int T, int window) {
+  const int tiles = attended_tiles(T, window);
   return tiles ? tiles + kPairCost : 0;
 }
 
@@ -832,10 +863,11 @@ struct StreamSmem {
   int64_t new_dst[kAppend ? kSegCap : 1];   // pool byte offset of the new row, or -1
 };
 
-template <int DT, int D, int G, bool kAppend>
+template <int DT, int D, int G, bool kAppend, bool kWindow>
 __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, G>;
   using SM = StreamSmem<DT, D, G, kAppend>;
+  const int window = kWindow ? a.window : 0;      // 0: every token
   constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
   constexpr int kRowBytes = GE::kRowBytes;
   __shared__ SM sm;
@@ -860,7 +892,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   for (int i = i0; i < i1; ++i) {
     const int T = min(max(a.context_lens[i], 0), a.max_context_len);
     sm.len[i] = T;
-    mine += pair_units(T);
+    mine += pair_units(T, window);
   }
   long long incl = mine;
 #pragma unroll
@@ -909,7 +941,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     int nseg = 0, ntot = 0;
     while (pos < hi && s < N && nseg < SM::kSegCap) {
       const int T = __builtin_amdgcn_readfirstlane(sm.len[s]);
-      const int units = pair_units(T);
+      const int units = pair_units(T, window);
       const int tiles = units - (units ? kPairCost : 0);
       const long long base = cum * Hkv;
       if (pos >= base + static_cast<long long>(units) * Hkv) {
@@ -937,7 +969,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       if (lane == 0) {
         sm.seg_seq[nseg] = s;
         sm.seg_g[nseg] = g;
-        sm.seg_tile0[nseg] = tile0;
+        sm.seg_tile0[nseg] = window_first(T, window) / kTileTokens + tile0;   // absolute
         sm.seg_start[nseg] = ntot;
         sm.seg_n[nseg] = n;
         sm.seg_flags[nseg] = flags | (pos == lo ? 0 : 4);
@@ -992,7 +1024,9 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       // the sequence's newest token is in this tile and comes from new_k/new_v
       const bool app = kAppend && t0 + live == T;
       const bool in_pool = entry == blk;
-      dmeta = live | (app ? kMetaAppend : 0) | (app && in_pool ? kMetaStore : 0) | (sg << 8);
+      const int first = kWindow ? max(0, window_first(T, window) - t0) : 0;   // rows before it
+      dmeta = live | (app ? kMetaAppend : 0) | (app && in_pool ? kMetaStore : 0) | (sg << 8) |
+              (first << 12);
     };
     auto tile_off = [&](int k) -> int64_t {
       const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff), k & 63);
@@ -1045,9 +1079,9 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     // slot in this launch: the descriptors of the tile stop short of it.
     auto put_new_row = [&](Keys& kr) {
       const int live = kr.meta & kMetaLive;
-      const char* nk = sm.newkv[kr.meta >> 8];
+      const char* nk = sm.newkv[(kr.meta >> 8) & 0xf];
       if (lane == 0)
-        sm.new_dst[kr.meta >> 8] =
+        sm.new_dst[(kr.meta >> 8) & 0xf] =
             (kr.meta & kMetaStore) ? kr.off + int64_t(live - 1) * kRowBytes : int64_t(-1);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
@@ -1068,7 +1102,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     if (ntot > 1) load_keys(1, KB);
     int cur = -1;
     auto step = [&](int k, Keys& kr) {
-      const int sg = kr.meta >> 8;
+      const int sg = (kr.meta >> 8) & 0xf;
       if (sg != cur) {               // a new segment begins
         cur = sg;
         tm.reset();
@@ -1076,9 +1110,11 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       }
       if constexpr (kAppend)
         if (kr.meta & kMetaAppend) put_new_row(kr);
+      const int first = kWindow ? (kr.meta >> 12) & 0xf : 0;
+      if (kWindow && first > 0) clear_rows_below(vr, first, rho);
       tm.stage_values(vr, sm.vtile);
       if (k + 1 < ntot) load_vals(k + 1);
-      tm.scores(a, kr.r, kr.meta & kMetaLive);
+      tm.scores(a, kr.r, first, kr.meta & kMetaLive);
       if (k + 2 < ntot) load_keys(k + 2, kr);
       tm.accumulate(sm.vtile);
       if (k + 1 == sm.seg_start[sg] + sm.seg_n[sg]) {   // the segment's last tile
@@ -1260,13 +1296,15 @@ __global__ __launch_bounds__(kWave * kPartitionWaves) void decode_partition_kern
     if (part == 0) zero_rows<DT, D>(a, row0, G);
     return;
   }
+  // partitions of tpp tiles from the tile holding the window's first position
+  const int s0 = window_first(T, a.window);
   const int tiles = (T + kTileTokens - 1) / kTileTokens;
   const int tpp = a.partition_tokens / kTileTokens;
-  const int lo = part * tpp;
+  const int lo = s0 / kTileTokens + part * tpp;
   if (lo >= tiles) return;
   const int hi = min(tiles, lo + tpp);
-  const int nparts = (tiles + tpp - 1) / tpp;
-  attend_segment<DT, D, G, kTileInBlock, NW>(a, sm, seq, g, T, lo, hi);
+  const int nparts = (attended_tiles(T, a.window) + tpp - 1) / tpp;
+  attend_segment<DT, D, G, kTileInBlock, NW>(a, sm, seq, g, T, s0, lo, hi);
   for (int idx = threadIdx.x; idx < G * D; idx += kWave * NW) {
     const int h = idx / D, d = idx - (idx / D) * D;
     float M, L, O;
@@ -1291,8 +1329,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
   const int g = blockIdx.x;
   const int seq = blockIdx.y;
   const int T = min(a.context_lens[seq], a.max_context_len);
-  const int P = a.partition_tokens;
-  const int nparts = T > 0 ? (T + P - 1) / P : 0;
+  const int tpp = a.partition_tokens / kTileTokens;
+  const int nparts = (attended_tiles(T, a.window) + tpp - 1) / tpp;
   if (nparts <= 1) return;
   const int NP = a.num_partitions;
   for (int idx = threadIdx.x; idx < G * D; idx += kMergeThreads) {
@@ -1378,15 +1416,23 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
     if constexpr (DT == PA_F32) {
       return hipErrorInvalidValue;
     } else {
-      const bool app = a.new_k != nullptr;
-      const void* k = app ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true>)
-                          : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false>);
-      const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 2 + (app ? 1 : 0), kWave);
+      // variants: appending decode, sliding window, plain (never both of the first two)
+      const int mode = a.new_k != nullptr ? 1 : a.window > 0 ? 2 : 0;
+      const void* k =
+          mode == 1 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true, false>)
+          : mode == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, true>)
+                      : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false>);
+      const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 4 + mode, kWave);
       if (W <= 0) return hipErrorInvalidDevice;
-      if (app)
-        launch_attention(decode_stream_kernel<DT, D, G, true>, dim3(W), dim3(kWave), stream, a);
+      if (mode == 1)
+        launch_attention(decode_stream_kernel<DT, D, G, true, false>, dim3(W), dim3(kWave),
+                         stream, a);
+      else if (mode == 2)
+        launch_attention(decode_stream_kernel<DT, D, G, false, true>, dim3(W), dim3(kWave),
+                         stream, a);
       else
-        launch_attention(decode_stream_kernel<DT, D, G, false>, dim3(W), dim3(kWave), stream, a);
+        launch_attention(decode_stream_kernel<DT, D, G, false, false>, dim3(W), dim3(kWave),
+                         stream, a);
       hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W),
                          dim3(MergeShape<G, D>::kThreads), 0, stream, a, W);
     }

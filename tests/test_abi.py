@@ -13,7 +13,8 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_workspace_bytes",
+    assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding",
+            "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
             "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
@@ -144,3 +145,20 @@ def test_append_decode_validation(nk, nv, kw, want):
 def test_profile_hook_without_launches():
     B.pa_profile_start()
     assert B.pa_profile_stop() == (0, 0.0)
+
+
+@pytest.mark.parametrize("window,kw,want", [
+    (0, {}, B.PA_ERR_INVALID_ARGUMENT),          # a window holds at least one token
+    (-5, {}, B.PA_ERR_INVALID_ARGUMENT),
+    (64, dict(hq=7), B.PA_ERR_INVALID_ARGUMENT),  # the decode's own checks
+    (64, dict(wsb=1 << 16), B.PA_ERR_WORKSPACE_TOO_SMALL),
+    (64, dict(n=0), B.PA_OK),
+])
+def test_sliding_validation(window, kw, want):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=8, cl=FAKE, n=4, maxlen=100, hq=8,
+             scale=0.1, out=FAKE, ws=FAKE, wsb=1 << 20, part=0)
+    a.update(kw)
+    d = desc()
+    assert B.lib().pa_decode_sliding(a["q"], a["k"], a["v"], ctypes.byref(d), a["bt"], a["mb"],
+                                     a["cl"], a["n"], a["maxlen"], a["hq"], a["scale"], window,
+                                     a["out"], a["ws"], a["wsb"], a["part"], None) == want
