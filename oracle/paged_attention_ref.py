@@ -43,6 +43,12 @@ Readings taken where the pages leave a step open:
 * Sliding window: the token being decoded (position ``T - 1``) is one of the
   last ``W`` tokens, so the keys are positions ``max(0, T - W) .. T - 1``; table
   entries of blocks wholly before them are never read.
+* Chunked prefill (same page, sections on the scheduler step and on long
+  prompts: a long prompt is read in chunks that run in one batch with other
+  requests' decode tokens).  A sequence brings ``M`` new query rows, the last
+  ``M`` of its ``T`` tokens (their K/V already written, as for a decode
+  token); row ``r`` sits at position ``T - M + r`` and attends to positions
+  ``0 .. T - M + r`` (causal).  A decode token is the case ``M = 1``.
 
 Parity pins (tests/test_oracle_pins.py): contiguous brute force, a torch
 float64 rendering of the page's sketch, placement invariance, shared-prefix
@@ -255,6 +261,52 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         for h in range(num_q_heads):
             g = kv_head_for_query_head(h, num_q_heads, num_kv_heads)
             out[i, h] = attend(q64[i, h], keys[:, g, :], values[:, g, :], sc)
+    return out
+
+
+def query_position(num_tokens: int, num_queries: int, r: int) -> int:
+    """Position of query row r of a chunk that ends the sequence's T tokens."""
+    return int(num_tokens) - int(num_queries) + int(r)
+
+
+def causal_keys(position: int) -> int:
+    """Keys a query at this position attends to: positions 0 .. position."""
+    return int(position) + 1
+
+
+def prefill(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+            block_tables: np.ndarray, context_lens, query_lens, scale: float,
+            dtype: str) -> np.ndarray:
+    """Causal attention of each sequence's last M_i tokens (a prompt chunk, or
+    one decode token) over its cached tokens; float64 out.
+
+    q: [sum M_i][Hq][D], sequence i's rows consecutive (sequence order);
+    context_lens: T_i, counting the chunk; query_lens: M_i, 0 <= M_i <= T_i.
+    """
+    num_rows, num_q_heads, head_dim = q.shape
+    _, num_kv_heads, block_size, pool_dim = k_pool.shape
+    if pool_dim != head_dim or v_pool.shape != k_pool.shape:
+        raise ValueError("q, k_pool and v_pool disagree on shapes")
+    if num_q_heads % num_kv_heads:
+        raise ValueError("query heads must be a multiple of kv heads")
+    lens = [int(x) for x in context_lens]
+    mq = [int(x) for x in query_lens]
+    if sum(mq) != num_rows or any(m < 0 or m > T for m, T in zip(mq, lens)):
+        raise ValueError("query lengths do not match q, or exceed the context")
+    sc = float(np.float32(scale))
+    q64 = to_float64(q, dtype)
+    out = np.zeros((num_rows, num_q_heads, head_dim), dtype=np.float64)
+    row = 0
+    for i, (T, M) in enumerate(zip(lens, mq)):
+        if M:
+            keys = gather_tokens(k_pool, block_tables[i], T, block_size, dtype)
+            values = gather_tokens(v_pool, block_tables[i], T, block_size, dtype)
+        for r in range(M):
+            n = causal_keys(query_position(T, M, r))
+            for h in range(num_q_heads):
+                g = kv_head_for_query_head(h, num_q_heads, num_kv_heads)
+                out[row + r, h] = attend(q64[row + r, h], keys[:n, g, :], values[:n, g, :], sc)
+        row += M
     return out
 
 

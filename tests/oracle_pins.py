@@ -434,6 +434,76 @@ def pin_window_blocks(o):
             assert (seen == bound) == ((W - 1) % B != 0)
 
 
+# ---------------------------------------------------------------------------
+# chunked prefill (a prompt chunk attends causally through the block table)
+# ---------------------------------------------------------------------------
+PREFILL_CASES = [
+    dict(seed=41, lens=[1, 5, 11, 16, 17, 40], mq=[1, 5, 3, 16, 1, 9], Hq=4, Hkv=2, D=8, B=4),
+    dict(seed=42, lens=[3, 33, 2, 6], mq=[2, 0, 2, 6], Hq=6, Hkv=3, D=6, B=2),
+    dict(seed=43, lens=[37, 64], mq=[20, 3], Hq=8, Hkv=1, D=4, B=8),
+]
+
+
+def _prefill_q(seed, mq, Hq, D):
+    return np.random.default_rng(seed + 1000).standard_normal((sum(mq), Hq, D)).astype(np.float32)
+
+
+def pin_prefill_bruteforce(o):
+    """Row r of a chunk of M rows ending at T attends to the first T - M + r + 1
+    tokens: the contiguous brute force over exactly those."""
+    for c in PREFILL_CASES:
+        q0, kp, vp, bt, lens, ck, cv = _tiny_problem(c["seed"], c["lens"], c["Hq"], c["Hkv"],
+                                                     c["D"], c["B"])
+        q = _prefill_q(c["seed"], c["mq"], c["Hq"], c["D"])
+        scale = float(np.float32(0.29))
+        got = o.prefill(q, kp, vp, bt, lens, c["mq"], scale, "f32")
+        G = c["Hq"] // c["Hkv"]
+        row = 0
+        for i, (T, M) in enumerate(zip(c["lens"], c["mq"])):
+            for r in range(M):
+                n = T - M + r + 1
+                want = np.array(_brute(q[row + r].tolist(), ck[i][:n].tolist(),
+                                       cv[i][:n].tolist(), scale, G))
+                np.testing.assert_allclose(got[row + r], want, rtol=1e-12, atol=1e-13)
+            row += M
+
+
+def pin_prefill_special_cases(o):
+    """One query per sequence is the decode step, bit for bit; a chunk's rows
+    do not depend on how the prompt was chunked; the first position of a
+    sequence returns its value row exactly; NaN in positions after a row's own
+    never reaches it (causality)."""
+    c = PREFILL_CASES[0]
+    q0, kp, vp, bt, lens, ck, cv = _tiny_problem(c["seed"], c["lens"], c["Hq"], c["Hkv"],
+                                                 c["D"], c["B"])
+    ones = [1 if T else 0 for T in c["lens"]]
+    dec = o.decode(q0, kp, vp, bt, lens, 0.3, "f32")
+    pre = o.prefill(q0[[i for i, T in enumerate(c["lens"]) if T]], kp, vp, bt, lens, ones, 0.3,
+                    "f32")
+    assert np.array_equal(pre, dec[[i for i, T in enumerate(c["lens"]) if T]])
+    # sequence 5 (40 tokens): its last 30 positions as one chunk, or as 10 + 20
+    T = c["lens"][5]
+    q = np.random.default_rng(7).standard_normal((30, c["Hq"], c["D"])).astype(np.float32)
+    one = o.prefill(q, kp, vp, bt[5:6], [T], [30], 0.3, "f32")
+    a = o.prefill(q[:10], kp, vp, bt[5:6], [T - 20], [10], 0.3, "f32")
+    b = o.prefill(q[10:], kp, vp, bt[5:6], [T], [20], 0.3, "f32")
+    assert np.array_equal(one, np.concatenate([a, b]))
+    # a whole prompt as one chunk: its row 0 is v_0 for every head
+    G = c["Hq"] // c["Hkv"]
+    whole = o.prefill(q[:5], kp, vp, bt[1:2], [5], [5], 0.3, "f32")
+    for h in range(c["Hq"]):
+        assert np.array_equal(whole[0, h], np.asarray(cv[1][0][h // G], dtype=np.float64))
+    # causality: poison every slot after position 9 of sequence 5
+    kp2, vp2 = kp.copy(), vp.copy()
+    for t in range(10, T):
+        blk, off = bt[5, t // c["B"]], t % c["B"]
+        kp2[blk, :, off, :] = np.nan
+        vp2[blk, :, off, :] = np.nan
+    early = o.prefill(q[:10], kp2, vp2, bt[5:6], [10], [10], 0.3, "f32")
+    assert np.isfinite(early).all()
+    assert np.array_equal(early, o.prefill(q[:10], kp, vp, bt[5:6], [10], [10], 0.3, "f32"))
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce,
     pin_page_sketch_torch,
@@ -451,4 +521,6 @@ ALL_PINS = [
     pin_window_bruteforce,
     pin_window_closed_forms,
     pin_window_blocks,
+    pin_prefill_bruteforce,
+    pin_prefill_special_cases,
 ]

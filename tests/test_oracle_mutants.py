@@ -95,6 +95,10 @@ def _gather_window_all(pool, table_row, first, num_tokens, block_size, dtype):
 
 
 MUTANTS["window_ignored_in_gather"] = ("gather_window", _gather_window_all)
+MUTANTS["prefill_excludes_own_key"] = ("causal_keys", lambda p: int(p))
+MUTANTS["prefill_sees_next_key"] = ("causal_keys", lambda p: int(p) + 2)
+MUTANTS["prefill_rows_from_start"] = ("query_position", lambda T, M, r: int(r))
+MUTANTS["prefill_rows_shifted"] = ("query_position", lambda T, M, r: int(T) - int(M) + int(r) - 1)
 
 
 def _run_pins():
