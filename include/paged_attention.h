@@ -203,11 +203,41 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                            int32_t partition_tokens, void* stream);
 
 /*
+ * pa_prefill -- causal attention of a prompt chunk through the block table
+ * (chunked prefill: "vLLM Framework and Inference Engine Design", scheduler
+ * step and "How does it support prompts of arbitrary length?": a long prompt
+ * is read in chunks that run in one batch with other requests' decode
+ * tokens).  Sequence i brings M_i = query_start[i+1] - query_start[i] query
+ * rows, its last M_i tokens (their K/V already written, e.g. by pa_write_kv);
+ * query row r sits at position T_i - M_i + r and attends to positions
+ * 0 .. T_i - M_i + r.  A decode token is M_i = 1; batches may mix both.
+ *
+ *   q, out        [query_start[num_seqs]][num_q_heads][head_dim], pool dtype;
+ *                 rows query_start[i] .. query_start[i+1] - 1 belong to
+ *                 sequence i.
+ *   query_start   int32 [num_seqs + 1], non-decreasing, query_start[0] = 0.
+ *   context_lens  T_i, counting the chunk; M_i <= T_i.
+ *   max_query_len host bound on every M_i (sizes the grid), at most
+ *                 max_context_len.
+ *
+ * Other arguments as pa_decode (no workspace).  16-bit pools only (fp32 pools
+ * return PA_ERR_UNSUPPORTED).  Contract violations clamp: M_i into [0, T_i],
+ * T_i into [0, max_context_len], table entries into the pool.
+ */
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const pa_pool_desc* pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t max_context_len,
+                     int32_t max_query_len, int32_t num_q_heads, float scale, void* out,
+                     void* stream);
+
+/*
  * pa_profile_start / pa_profile_stop -- kernel timing for measurements; not
- * needed to compute anything.  Between the two calls, every pa_decode and
- * pa_append_decode launches its attention kernel (the balanced-split stream
- * kernel, or the fixed-partition kernel) with a HIP start and stop event
- * attached to that dispatch; the piece merge is not included.  pa_profile_stop
+ * needed to compute anything.  Between the two calls, every pa_decode,
+ * pa_append_decode, pa_decode_sliding and pa_prefill call launches its
+ * attention kernel (the balanced-split stream kernel, the fixed-partition
+ * kernel, or the prefill kernel) with a HIP start and stop event attached to
+ * that dispatch; the piece merge is not included.  pa_profile_stop
  * turns timing off, waits for the recorded events, and returns how many
  * launches were timed and their mean duration in microseconds (0 launches:
  * mean 0).  The switch is process-wide; while it is on each call creates two

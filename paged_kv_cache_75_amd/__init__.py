@@ -4,6 +4,7 @@
     pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, ...)
     pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, ...)
     pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, window, ...)
+    pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, ...)
 
 The functions marshal torch tensors into libpa.so (built in-tree by
 ``paged_kv_cache_75_amd.build``).  They raise RuntimeError when the library is
@@ -12,13 +13,13 @@ missing; nothing falls back to another implementation.
 from .binding import (PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED,
                       PA_ERR_WORKSPACE_TOO_SMALL, PA_F16, PA_F32, PA_OK, PaError, lib,
                       pa_append_decode, pa_decode, pa_decode_sliding,
-                      pa_decode_workspace_bytes, pa_pool_desc,
+                      pa_decode_workspace_bytes, pa_pool_desc, pa_prefill,
                       pa_profile_start, pa_profile_stop, pa_status_string, pa_write_kv,
                       pool_desc)
 
 __all__ = ["PA_BF16", "PA_ERR_HIP", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED",
            "PA_ERR_WORKSPACE_TOO_SMALL", "PA_F16", "PA_F32", "PA_OK", "PaError", "lib",
            "pa_append_decode", "pa_decode", "pa_decode_sliding", "pa_decode_workspace_bytes",
-           "pa_pool_desc",
+           "pa_pool_desc", "pa_prefill",
            "pa_profile_start", "pa_profile_stop", "pa_status_string", "pa_write_kv",
            "pool_desc"]

@@ -70,6 +70,8 @@ def lib():
                                i32, vp, vp, sz, i32, vp], c_int),
         "pa_append_decode": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
                               ctypes.c_float, vp, vp, sz, i32, vp], c_int),
+        "pa_prefill": ([vp, vp, vp, desc, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
+                        vp, vp], c_int),
         "pa_profile_start": ([], c_int),
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
@@ -195,6 +197,48 @@ def pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, wind
     trained with sliding-window attention)."""
     return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
                    max_context_len, workspace, partition_tokens, stream, window=int(window))
+
+
+def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None,
+               max_context_len=None, max_query_len=None, stream=None):
+    """Causal attention of each sequence's last M_i tokens (a prompt chunk or
+    a decode token): q and out are [query_start[-1]][Hq][D]; rows
+    query_start[i] .. query_start[i+1]-1 belong to sequence i.  The host
+    bounds are read from the device when omitted (a synchronizing copy)."""
+    torch = _torch()
+    desc = pool_desc(k_pool)
+    dev = k_pool.device
+    _check(k_pool, "k_pool")
+    _check(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(q, "q", dtype=k_pool.dtype, dim=3, device=dev)
+    _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    _check(query_start, "query_start", dtype=torch.int32, dim=1, device=dev)
+    n = int(context_lens.shape[0])
+    rows, hq, d = (int(x) for x in q.shape)
+    if d != desc.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if int(block_tables.shape[0]) != n or int(query_start.shape[0]) != n + 1:
+        raise ValueError("block_tables rows must equal num_seqs, query_start num_seqs + 1")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if n else 0
+    if max_query_len is None:
+        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if n else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, device=dev)
+    if tuple(out.shape) != (rows, hq, d):
+        raise ValueError("out must have q's shape")
+    st = lib().pa_prefill(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), ctypes.byref(desc),
+                          block_tables.data_ptr(), int(block_tables.shape[1]),
+                          context_lens.data_ptr(), query_start.data_ptr(), n,
+                          int(max_context_len), int(max_query_len), hq, float(scale),
+                          out.data_ptr(), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_prefill")
+    return out
 
 
 def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,

@@ -138,6 +138,45 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                 workspace_bytes, partition_tokens, 0, stream);
 }
 
+pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
+                     const pa_pool_desc* pool, const int32_t* block_tables,
+                     int32_t max_blocks_per_seq, const int32_t* context_lens,
+                     const int32_t* query_start, int32_t num_seqs, int32_t max_context_len,
+                     int32_t max_query_len, int32_t num_q_heads, float scale, void* out,
+                     void* stream) {
+  int32_t group = 0;
+  pa_status s = pa::check_prefill(num_seqs, num_q_heads, pool, max_context_len,
+                                  max_blocks_per_seq, max_query_len, &group);
+  if (s != PA_OK) return s;
+  s = pa::check_decode_pointers(q, k_pool, v_pool, block_tables, context_lens, out, num_seqs);
+  if (s != PA_OK) return s;
+  if (num_seqs > 0 && !query_start) return PA_ERR_INVALID_ARGUMENT;
+  if (!std::isfinite(scale)) return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs == 0 || max_query_len == 0) return PA_OK;
+  pa::DecodeArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.num_blocks = pool->num_blocks;
+  int32_t lb = 0;
+  while ((1 << lb) < pool->block_size) ++lb;
+  a.log2_block = lb;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  a.query_start = query_start;
+  a.max_query_len = max_query_len;
+  const hipError_t e = pa::launch_prefill(a, pool->dtype, pool->head_dim, group,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
 pa_status pa_profile_start(void) {
   pa::profile_start();
   return PA_OK;

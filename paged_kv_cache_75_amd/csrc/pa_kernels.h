@@ -56,9 +56,18 @@ struct DecodeArgs {
   const void* new_k;
   const void* new_v;
   int32_t window;           // sliding window in tokens; 0: attend to every token
+  // Chunked prefill: rows query_start[i] .. query_start[i+1]-1 of q (and of
+  // out) are sequence i's queries, the last M_i of its T_i tokens.
+  const int32_t* query_start;
+  int32_t max_query_len;    // host bound on M_i (sizes the grid)
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+
+// Chunked prefill (16-bit pools): causal attention of each sequence's last
+// M_i tokens; group as planned.
+hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, int32_t group,
+                          hipStream_t stream);
 
 // Kernel timing (measurement only): start attaching events to the attention
 // kernel of each decode call; stop, wait for those events and report.

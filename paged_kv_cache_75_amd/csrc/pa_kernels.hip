@@ -1355,6 +1355,153 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------
 // launch
 // ---------------------------------------------------------------------------
+// Chunked prefill: causal attention of each sequence's last M tokens (a prompt
+// chunk; a decode token is M = 1).  One wave per (query block, kv head,
+// sequence).  A query block fills the 16 columns of the MFMA operand that
+// holds Q^T: kQueries = 16 / G queries times the G heads of the kv head, so
+// the key and value tiles read for it serve all of them.  Column c is query
+// r = c / G of the block (head c % G) at position T - M + r; key rows after
+// that position get weight zero (its per-lane `live` bound), and the wave
+// streams the tiles up to the block's last position with the decode kernels'
+// tile math and prefetching.
+// ---------------------------------------------------------------------------
+template <int G>
+struct PrefillShape {
+  static constexpr int kQueries = 16 / G;
+  static constexpr int kCols = kQueries * G;
+};
+
+template <int DT, int D, int G, bool kTileInBlock>
+__global__ __launch_bounds__(kWave) void prefill_kernel(DecodeArgs a) {
+  using GE = Geo<DT, D, 16>;
+  constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
+  constexpr int kRowBytes = GE::kRowBytes;
+  constexpr int QB = PrefillShape<G>::kQueries;
+  using TM = MfmaPv<DT, D, 16>;
+  __shared__ __align__(16) char vtile[TM::kScratchBytes];
+
+  const int seq = blockIdx.z;
+  const int g = blockIdx.y;
+  const int lane = threadIdx.x;
+  const int T = min(max(a.context_lens[seq], 0), a.max_context_len);
+  const int row_begin = a.query_start[seq];
+  const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
+  const int r0 = blockIdx.x * QB;
+  if (r0 >= M) return;
+  const int nq = min(QB, M - r0);
+
+  TM tm;
+  tm.set_lane(lane);
+  const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
+  const bool col_ok = c < nq * G;
+  const int qr = r0 + (col_ok ? c / G : 0);                 // query row of this column
+  const int head = g * G + (col_ok ? c % G : 0);
+  const int pos = T - M + qr;                               // its position
+  const int64_t out_row = int64_t(row_begin + qr) * a.num_q_heads + head;
+  const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                     out_row * kRowBytes);
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk) tm.qb[kk] = col_ok ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+  tm.reset();
+
+  const int ntiles = (T - M + r0 + nq - 1) / kTileTokens + 1;   // up to the last position
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
+  const int64_t head_rows = int64_t(g) << lb;
+  const int64_t blk_rows = int64_t(a.num_kv_heads) << lb;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int nblk = a.num_blocks;
+  const int k_off = c * kRowBytes + gq * 16;
+  const int v_off = rho * kRowBytes + chi * 16;
+
+  // tile k's block (one per lane, 64 tiles per load) when tiles lie in blocks
+  int tbl = 0;
+  auto load_tbl = [&](int batch) {
+    const int k = min(64 * batch + lane, ntiles - 1);
+    tbl = min(max(table[(k * kTileTokens) >> lb], 0), nblk - 1);
+  };
+  auto tile_byte = [&](int k) -> int64_t {
+    const int64_t blk = __builtin_amdgcn_readlane(tbl, k & 63);
+    return (blk * blk_rows + head_rows + ((k * kTileTokens) & bmask)) * kRowBytes;
+  };
+  auto rsrc = [&](const char* base, int k) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + tile_byte(k)), 0,
+                                             min(kTileTokens, T - k * kTileTokens) * kRowBytes,
+                                             kBufferDword3);
+  };
+  // blocks smaller than a tile: each lane finds its row's block; rows past
+  // T - 1 read row T - 1 (weight zero)
+  auto row_of = [&](int t0, int dt) -> int64_t {
+    const int t = t0 + min(dt, T - 1 - t0);
+    const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
+    return blk * blk_rows + head_rows + (t & bmask);
+  };
+  auto load_keys = [&](int k, KeyRegs<DT, D>& r) {
+    if constexpr (kTileInBlock) {
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, k);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        r.k[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
+    } else {
+      const uint4* kp = reinterpret_cast<const uint4*>(kbase + row_of(k * kTileTokens, c) * kRowBytes);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) r.k[kk] = kp[4 * kk + gq];
+    }
+  };
+  auto load_values = [&](int k, ValRegs<DT, D>& r) {
+    if constexpr (kTileInBlock) {
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, k);
+#pragma unroll
+      for (int s2 = 0; s2 < VS; ++s2)
+        r.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                rv, v_off + s2 * RPI * kRowBytes, 0, 0));
+    } else {
+#pragma unroll
+      for (int s2 = 0; s2 < VS; ++s2)
+        r.v[s2] = reinterpret_cast<const uint4*>(
+            vbase + row_of(k * kTileTokens, s2 * RPI + rho) * kRowBytes)[chi];
+    }
+  };
+
+  if constexpr (kTileInBlock) load_tbl(0);
+  KeyRegs<DT, D> KA, KB;
+  ValRegs<DT, D> VR;
+  load_keys(0, KA);
+  load_values(0, VR);
+  if (ntiles > 1) load_keys(1, KB);
+  auto step = [&](int k, KeyRegs<DT, D>& kr) {
+    tm.stage_values(VR, vtile);
+    if (k + 1 < ntiles) load_values(k + 1, VR);
+    // keys at positions 16k .. pos of this column take part
+    const int live = col_ok ? min(kTileTokens, max(0, pos - k * kTileTokens + 1)) : 0;
+    tm.scores(a, kr, 0, live);
+    if (k + 2 < ntiles) {
+      if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
+      load_keys(k + 2, kr);
+    }
+    tm.accumulate(vtile);
+  };
+  for (int k = 0; k < ntiles; k += 2) {
+    step(k, KA);
+    if (k + 1 >= ntiles) break;
+    step(k + 1, KB);
+  }
+
+  // column c's sum is spread over its four lanes (gq = 0..3)
+  float l = tm.l_run;
+  l += __shfl_xor(l, 16, kWave);
+  l += __shfl_xor(l, 32, kWave);
+  if (col_ok) {
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int n = 0; n < TM::NT; ++n)
+      store4<DT>(a.out, out_row * D + 16 * n + 4 * gq, tm.o[n] * inv);
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Workgroups of `kernel` the device keeps resident at once (cached per device).
 int resident_workgroups(const void* kernel, int kernel_id, int threads) {
   static std::mutex mu;
@@ -1521,6 +1668,61 @@ hipError_t profile_stop(int32_t* launches, double* mean_us) {
   *launches = n;
   *mean_us = n ? total_ms * 1e3 / n : 0.0;
   return err;
+}
+
+namespace {
+
+template <int DT, int D, int G>
+hipError_t launch_prefill_g(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (DT == PA_F32) {
+    return hipErrorInvalidValue;
+  } else {
+    const dim3 grid((a.max_query_len + PrefillShape<G>::kQueries - 1) / PrefillShape<G>::kQueries,
+                    a.num_kv_heads, a.num_seqs);
+    if (a.log2_block >= 4)
+      launch_attention(prefill_kernel<DT, D, G, true>, grid, dim3(kWave), stream, a);
+    else
+      launch_attention(prefill_kernel<DT, D, G, false>, grid, dim3(kWave), stream, a);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_prefill_d(const DecodeArgs& a, int32_t group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_prefill_g<DT, D, 1>(a, stream);
+    case 2: return launch_prefill_g<DT, D, 2>(a, stream);
+    case 3: return launch_prefill_g<DT, D, 3>(a, stream);
+    case 4: return launch_prefill_g<DT, D, 4>(a, stream);
+    case 5: return launch_prefill_g<DT, D, 5>(a, stream);
+    case 6: return launch_prefill_g<DT, D, 6>(a, stream);
+    case 7: return launch_prefill_g<DT, D, 7>(a, stream);
+    case 8: return launch_prefill_g<DT, D, 8>(a, stream);
+    case 16: return launch_prefill_g<DT, D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_prefill_dt(const DecodeArgs& a, int32_t head_dim, int32_t group,
+                             hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_prefill_d<DT, 64>(a, group, stream);
+    case 128: return launch_prefill_d<DT, 128>(a, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, int32_t group,
+                          hipStream_t stream) {
+  if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
+  switch (dtype) {
+    case PA_F16: return launch_prefill_dt<PA_F16>(a, head_dim, group, stream);
+    case PA_BF16: return launch_prefill_dt<PA_BF16>(a, head_dim, group, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {

@@ -116,6 +116,20 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
   return PA_OK;
 }
 
+pa_status check_prefill(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc* pool,
+                        int32_t max_context_len, int32_t max_blocks_per_seq,
+                        int32_t max_query_len, int32_t* group) {
+  DecodePlan p;   // the decode's shape checks (any valid partition)
+  const pa_status s = plan_decode(num_seqs, num_q_heads, pool, max_context_len,
+                                  max_blocks_per_seq, kTileTokens, &p);
+  if (s != PA_OK) return s;
+  if (max_blocks_per_seq <= 0 && num_seqs > 0) return PA_ERR_INVALID_ARGUMENT;
+  if (max_query_len < 0 || max_query_len > max_context_len) return PA_ERR_INVALID_ARGUMENT;
+  if (pool->dtype == PA_F32) return PA_ERR_UNSUPPORTED;   // matrix-core tile math only
+  *group = p.group;
+  return PA_OK;
+}
+
 pa_status check_decode_pointers(const void* q, const void* k_pool, const void* v_pool,
                                 const int32_t* block_tables, const int32_t* context_lens,
                                 const void* out, int32_t num_seqs) {

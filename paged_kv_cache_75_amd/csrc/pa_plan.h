@@ -46,6 +46,11 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
                       int32_t max_context_len, int32_t max_blocks_per_seq,
                       int32_t partition_tokens, DecodePlan* plan);
 
+// Shape checks for chunked prefill; sets the query heads per kv head.
+pa_status check_prefill(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc* pool,
+                        int32_t max_context_len, int32_t max_blocks_per_seq,
+                        int32_t max_query_len, int32_t* group);
+
 pa_status check_decode_pointers(const void* q, const void* k_pool, const void* v_pool,
                                 const int32_t* block_tables, const int32_t* context_lens,
                                 const void* out, int32_t num_seqs);

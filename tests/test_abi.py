@@ -13,7 +13,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so
 
 def test_exports_every_declared_function():
     names = B.declared_functions()
-    assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding",
+    assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding", "pa_prefill",
             "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
             "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
@@ -162,3 +162,27 @@ def test_sliding_validation(window, kw, want):
     assert B.lib().pa_decode_sliding(a["q"], a["k"], a["v"], ctypes.byref(d), a["bt"], a["mb"],
                                      a["cl"], a["n"], a["maxlen"], a["hq"], a["scale"], window,
                                      a["out"], a["ws"], a["wsb"], a["part"], None) == want
+
+
+def prefill(d, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=8, cl=FAKE, qs=FAKE, n=4, maxlen=100, maxq=64,
+             hq=8, scale=0.1, out=FAKE)
+    a.update(kw)
+    return B.lib().pa_prefill(a["q"], a["k"], a["v"], ctypes.byref(d) if d is not None else None,
+                              a["bt"], a["mb"], a["cl"], a["qs"], a["n"], a["maxlen"], a["maxq"],
+                              a["hq"], a["scale"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,dt,want", [
+    (dict(qs=None), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(maxq=101), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),    # more queries than tokens
+    (dict(maxq=-1), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(hq=7), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(mb=0), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(scale=float("inf")), B.PA_BF16, B.PA_ERR_INVALID_ARGUMENT),
+    (dict(), B.PA_F32, B.PA_ERR_UNSUPPORTED),                 # matrix-core tile math only
+    (dict(n=0), B.PA_BF16, B.PA_OK),
+    (dict(maxq=0), B.PA_F16, B.PA_OK),
+])
+def test_prefill_validation(kw, dt, want):
+    assert prefill(desc(dt=dt), **kw) == want

@@ -421,3 +421,61 @@ def test_sliding_window_covering_everything_is_pa_decode():
                                       max_context_len=dw.max_context_len,
                                       partition_tokens=part), w.dtype)
         assert np.array_equal(_bytes(a), _bytes(b))
+
+
+# ---------------------------------------------------------------------------
+# pa_prefill: causal attention of each sequence's last M_i tokens
+# ---------------------------------------------------------------------------
+def _prefill_case(w, mq, seed, label, sample_rows=None):
+    import torch
+    from workloads.generate import round_to_dtype
+    from paged_kv_cache_75_amd import pa_prefill, pa_write_kv
+    rng = np.random.default_rng(seed)
+    q = round_to_dtype(rng.standard_normal((int(sum(mq)), w.num_q_heads, w.head_dim))
+                       .astype(np.float32), w.dtype)
+    qs = np.concatenate([[0], np.cumsum(mq)]).astype(np.int32)
+    dw = upload(w, DEV)
+    say(f"[prefill] {label}: {len(mq)} seqs, {int(sum(mq))} query rows")
+    pa_write_kv(dw.new_k, dw.new_v, dw.slot_mapping, dw.k_pool, dw.v_pool)
+    from gpu_util import to_device
+    out = pa_prefill(to_device(q, w.dtype, DEV), dw.k_pool, dw.v_pool, dw.block_tables,
+                     dw.context_lens, to_device(qs, None, DEV), w.scale,
+                     max_context_len=w.max_context_len, max_query_len=int(max(mq)))
+    _sync()
+    k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size,
+                        inplace=sample_rows is not None)
+    got = to_f64(out)
+    if sample_rows is None:
+        want = ref.prefill(q, k, v, w.block_tables, w.context_lens, mq, w.scale, w.dtype)
+        compare(got, want, w.dtype, label=label)
+    else:
+        # sequences picked whole: the oracle runs on those only
+        for i in sample_rows:
+            want = ref.prefill(q[qs[i]:qs[i + 1]], k, v, w.block_tables[i:i + 1],
+                               w.context_lens[i:i + 1], [mq[i]], w.scale, w.dtype)
+            compare(got[qs[i]:qs[i + 1]], want, w.dtype, label=f"{label} seq {i}")
+
+
+PREFILL_SHAPES = [("bf16", 16, 4, 128), ("f16", 16, 7, 64), ("f16", 8, 1, 128), ("bf16", 32, 16, 128)]
+
+
+@pytest.mark.parametrize("dtype,block_size,group,head_dim", PREFILL_SHAPES,
+                         ids=[f"{d}-B{b}-G{g}-D{h}" for d, b, g, h in PREFILL_SHAPES])
+def test_prefill_mixed_batch(dtype, block_size, group, head_dim):
+    """Prompt chunks of 1 (a decode token), 3, 16, 17, 40 tokens and whole
+    prompts, in one batch with empty ones, against the oracle."""
+    hkv = 2 if group < 16 else 1
+    lens = [1, 5, 16, 17, 40, 100, 33, 0, 257, 64]
+    mq = [1, 3, 16, 17, 40, 1, 33, 0, 17, 64]
+    w = workloads.random_paged("prefill", dtype, hkv * group, hkv, head_dim, block_size, lens,
+                               seed=1800 + group + block_size, spare_frac=0.1)
+    _prefill_case(w, mq, 1900 + group, f"{dtype} B={block_size} G={group} D={head_dim}")
+
+
+def test_prefill_full_size():
+    """Sixteen Llama-3-8B sequences, each a 512-token chunk at the end of a
+    lognormal context (the prefill bench's batch); four sequences checked
+    whole against the oracle."""
+    w = workloads.make(3, seed=2000, num_seqs=16)
+    mq = [min(512, int(T)) for T in w.context_lens]
+    _prefill_case(w, mq, 2001, "llama3-8b prefill", sample_rows=[0, 5, 10, 15])
