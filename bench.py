@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, vendor figure
 
 WORKLOAD_NAMES = {
     1: "tiny-decode-f32: 4 seqs, 4q/4kv heads, d64, B4, lens [7,8,9,8]",
@@ -53,6 +54,9 @@ def parse():
                          "and pa_write_kv + pa_decode (both), or only one of them")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (pa_decode_sliding; 0 = full attention)")
+    ap.add_argument("--prefill", type=int, default=0,
+                    help="chunked prefill instead of decode: every sequence of the first 16 of "
+                         "the Llama-3-8B batch gets a chunk of this many new tokens (pa_prefill)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -130,6 +134,106 @@ def kv_bytes_per_step(w, window: int = 0) -> int:
     return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(lens.sum())
 
 
+def prefill_main(args):
+    """Chunked prefill: each of 16 Llama-3-8B-shaped sequences (the first 16
+    lengths of the decode batch, seed 3) gets a chunk of args.prefill new
+    tokens.  Step = pa_write_kv of every chunk token + pa_prefill.  Work unit:
+    one (query row, attended key) pair per query head, 4 * D flops (QK^T and
+    P.V); bound by the matrix cores."""
+    import numpy as np
+    import torch
+
+    import workloads
+    from workloads.generate import round_to_dtype
+    from paged_kv_cache_75_amd import (pa_prefill, pa_profile_start, pa_profile_stop,
+                                       pa_write_kv)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    M = args.prefill
+    base = workloads.make(3, seed=3, poison=False).context_lens[:16]
+    lens = [int(T) + M for T in base]
+    w = workloads.random_paged("llama3-8b-prefill", "bf16", 32, 8, 128, 16, lens, seed=args.seed or 3,
+                               poison=False)
+    rng = np.random.default_rng(11)
+    n = len(lens)
+    q = round_to_dtype(rng.standard_normal((n * M, 32, 128)).astype(np.float32), "bf16")
+    ck = round_to_dtype(rng.standard_normal((n * M, 8, 128)).astype(np.float32), "bf16")
+    cv = round_to_dtype(rng.standard_normal((n * M, 8, 128)).astype(np.float32), "bf16")
+    slots = np.array([int(w.block_tables[i, t // 16]) * 16 + t % 16
+                      for i, T in enumerate(lens) for t in range(T - M, T)], dtype=np.int32)
+
+    def up(a, bf16):
+        a = np.ascontiguousarray(a)
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16) if bf16 else torch.from_numpy(a)
+        return t.to(dev)
+
+    dq, dck, dcv, dslots = up(q, True), up(ck, True), up(cv, True), up(slots, False)
+    kp, vp = up(w.k_pool, True), up(w.v_pool, True)
+    bt, cl = up(w.block_tables.astype(np.int32), False), up(np.array(lens, np.int32), False)
+    qs = up(np.arange(0, (n + 1) * M, M, dtype=np.int32), False)
+    out = torch.empty_like(dq)
+    maxlen = max(lens)
+
+    def step():
+        pa_write_kv(dck, dcv, dslots, kp, vp)
+        pa_prefill(dq, kp, vp, bt, cl, qs, w.scale, out=out, max_context_len=maxlen,
+                   max_query_len=M)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pa_profile_start()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    launches, kernel_us = pa_profile_stop()
+    pairs = sum(T - M + r + 1 for T in lens for r in range(M))       # (query, key) pairs
+    flops = 4 * 32 * 128 * pairs
+    kv_bytes = 2 * 8 * 128 * 2 * sum(lens)
+    achieved = flops / (kernel_us * 1e-6) / 1e12
+    result = {
+        "metric": "chunked prefill attention: TFLOP/s (bf16 matrix cores), us/step",
+        "value": round(flops / (ms * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3-8b-prefill-bf16: 16 seqs, 32q/8kv heads, d128, B16, "
+                               f"a {M}-token chunk after each of the first 16 decode-batch contexts",
+                   "query_rows": n * M, "attended_pairs_per_head": pairs,
+                   "flops_per_step": flops, "kv_bytes_per_step": kv_bytes,
+                   "step_calls": "pa_write_kv (chunk tokens) + pa_prefill"},
+        "roofline": {"bound": "mfma", "kernel": "prefill_kernel (attention kernel of pa_prefill)",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": None, "kernel_us_mean": round(kernel_us, 2),
+                     "kernel_launches_timed": launches},
+    }
+    if not args.no_cpu_baseline:
+        import oracle.paged_attention_ref as ref
+        from threadpoolctl import threadpool_limits
+        k, v = ref.write_kv(w.k_pool, w.v_pool, ck, cv, slots, 16)
+        done, secs, i = 0, 0.0, 0
+        with threadpool_limits(1):
+            while secs < args.cpu_seconds and i < n:
+                t = time.perf_counter()
+                ref.prefill(q[i * M:(i + 1) * M], k, v, w.block_tables[i:i + 1], [lens[i]], [M],
+                            w.scale, "bf16")
+                secs += time.perf_counter() - t
+                done += 4 * 32 * 128 * sum(lens[i] - M + r + 1 for r in range(M))
+                i += 1
+        result["cpu_baseline"] = {"value": round(done / secs / 1e12, 6), "unit": "TFLOP/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{i} of the {n} sequences' chunks, {secs:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -150,6 +254,9 @@ def main():
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
+    if args.prefill:
+        prefill_main(args)
+        return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cfg = args.config
