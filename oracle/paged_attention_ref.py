@@ -43,6 +43,15 @@ Readings taken where the pages leave a step open:
 * Sliding window: the token being decoded (position ``T - 1``) is one of the
   last ``W`` tokens, so the keys are positions ``max(0, T - W) .. T - 1``; table
   entries of blocks wholly before them are never read.
+* FP8 KV cache (same page, the engine settings: ``kv_cache_dtype="fp8"``
+  halves the KV memory; the besthub page, "Quantization: Reducing Weight & KV
+  Precision": ``--kv-cache-dtype fp8`` stores the KV cache in FP8).  The
+  format and scale are not on the pages (readings): OCP 8-bit floating point
+  E4M3 (the published OFP8 definition: sign, 4 exponent bits with bias 7,
+  3 mantissa bits, largest finite 448, no infinities, S.1111.111 is NaN) with
+  one float32 scale per pool: a code is E4M3 of ``float32(x) /
+  float32(scale)``, rounded to nearest even and saturated to +-448; its value
+  is the decoded code times the scale.
 * Chunked prefill (same page, sections on the scheduler step and on long
   prompts: a long prompt is read in chunks that run in one batch with other
   requests' decode tokens).  A sequence brings ``M`` new query rows, the last
@@ -62,7 +71,52 @@ import numpy as np
 
 # dtype tags shared by the inputs: 'f32' and 'f16' are NumPy float arrays;
 # 'bf16' arrays hold the raw 16-bit patterns as uint16 (NumPy has no bfloat16).
-DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2}
+DTYPE_BYTES = {"f32": 4, "f16": 2, "bf16": 2, "fp8e4m3": 1}
+
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    """Exact float64 value of E4M3 codes (uint8): normal 2^(E-7) * (1 + m/8),
+    subnormal (E = 0) m * 2^-9, S.1111.111 NaN."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where(c & 0x80, -1.0, 1.0)
+    E = (c >> 3) & 0xF
+    m = c & 0x7
+    mag = np.where(E == 0, m * 2.0 ** -9, np.ldexp(1.0 + m / 8.0, E - 7))
+    out = sign * mag
+    return np.where((E == 15) & (m == 7), np.nan, out)
+
+
+def fp8_e4m3_encode(y) -> np.ndarray:
+    """E4M3 code of float32 values: round to nearest, ties to an even
+    mantissa; magnitudes of 448 and above (infinities too) saturate to 448;
+    NaN gives S.1111.111."""
+    y = np.asarray(y, dtype=np.float32)
+    sign = (np.signbit(y).astype(np.int64) << 7)
+    a = np.abs(y.astype(np.float64))
+    nan = np.isnan(a)
+    a = np.minimum(np.where(nan, 0.0, a), 2.0 * FP8_E4M3_MAX)   # all of these saturate
+    # normal range: a = 2^e * f with f in [1, 2)
+    frac, exp = np.frexp(np.where(a > 0, a, 1.0))
+    e = exp - 1
+    q = np.rint((frac * 2.0 - 1.0) * 8.0).astype(np.int64)        # half to even
+    e = np.where(q == 8, e + 1, e)
+    q = np.where(q == 8, 0, q)
+    normal = ((e + 7) << 3) | q
+    # subnormal range: multiples of 2^-9 (8 rounds up into the first normal)
+    sub = np.rint(a * 2.0 ** 9).astype(np.int64)
+    code = np.where(a < 2.0 ** -6, sub, normal)
+    code = np.where(a >= FP8_E4M3_MAX, 0x7E, code)
+    code = np.where(nan, 0x7F, code)
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_fp8(x: np.ndarray, dtype: str, scale: float) -> np.ndarray:
+    """Codes stored for elements x (of ``dtype``) in a pool with this scale."""
+    x32 = to_float64(x, dtype).astype(np.float32)      # exact for every dtype here
+    return fp8_e4m3_encode(x32 / np.float32(scale))
 
 
 # ---------------------------------------------------------------------------
@@ -74,6 +128,8 @@ def to_float64(arr: np.ndarray, dtype: str) -> np.ndarray:
     A bfloat16 number is the upper half of a float32, so its bit pattern
     shifted left by 16 is that float32; fp16 and fp32 widen exactly.
     """
+    if dtype == "fp8e4m3":
+        return fp8_e4m3_decode(arr)
     if dtype == "bf16":
         if arr.dtype != np.uint16:
             raise TypeError("bf16 arrays are carried as uint16 bit patterns")
@@ -119,6 +175,15 @@ def slot_of_token(table_row, t: int, block_size: int) -> int:
 def slot_location(slot: int, block_size: int) -> tuple[int, int]:
     """Inverse of the slot formula: (physical block, offset) of a slot."""
     return slot // block_size, slot % block_size
+
+
+def write_kv_fp8(k_pool: np.ndarray, v_pool: np.ndarray, k: np.ndarray, v: np.ndarray,
+                 slot_mapping, block_size: int, dtype: str, k_scale: float, v_scale: float,
+                 inplace: bool = False):
+    """The slot write into FP8 pools (uint8 codes): the new rows, of
+    ``dtype``, quantized with the pools' scales."""
+    return write_kv(k_pool, v_pool, quantize_fp8(k, dtype, k_scale),
+                    quantize_fp8(v, dtype, v_scale), slot_mapping, block_size, inplace=inplace)
 
 
 def kv_head_for_query_head(h: int, num_q_heads: int, num_kv_heads: int) -> int:
@@ -227,7 +292,8 @@ def attend(q_h: np.ndarray, keys: np.ndarray, values: np.ndarray,
 
 def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
            block_tables: np.ndarray, context_lens, scale: float,
-           dtype: str, seqs=None, window=None) -> np.ndarray:
+           dtype: str, seqs=None, window=None, kv_dtype=None, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> np.ndarray:
     """Decode-step attention for every (sequence, query head); float64 out.
 
     q: [N][Hq][D]; pools: [num_blocks][Hkv][B][D]; block_tables: int [N][MB];
@@ -235,6 +301,8 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
     the pool).  ``seqs`` restricts the work to some sequences (their rows of the
     result are filled, the others are left NaN) for sampled checks at full size.
     ``window``: a sliding window of that many tokens (None: full attention).
+    ``kv_dtype``: the pools' element type when it differs from q's (FP8 pools,
+    "fp8e4m3", hold codes whose values are multiplied by k_scale / v_scale).
     """
     num_seqs, num_q_heads, head_dim = q.shape
     _, num_kv_heads, block_size, pool_dim = k_pool.shape
@@ -251,13 +319,17 @@ def decode(q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
         if T == 0:
             out[i] = 0.0
             continue
+        pool_dtype = dtype if kv_dtype is None else kv_dtype
         if window is None:
-            keys = gather_tokens(k_pool, block_tables[i], T, block_size, dtype)
-            values = gather_tokens(v_pool, block_tables[i], T, block_size, dtype)
+            keys = gather_tokens(k_pool, block_tables[i], T, block_size, pool_dtype)
+            values = gather_tokens(v_pool, block_tables[i], T, block_size, pool_dtype)
         else:
             first = window_start(T, window)
-            keys = gather_window(k_pool, block_tables[i], first, T, block_size, dtype)
-            values = gather_window(v_pool, block_tables[i], first, T, block_size, dtype)
+            keys = gather_window(k_pool, block_tables[i], first, T, block_size, pool_dtype)
+            values = gather_window(v_pool, block_tables[i], first, T, block_size, pool_dtype)
+        if kv_dtype is not None:
+            keys = keys * float(np.float32(k_scale))
+            values = values * float(np.float32(v_scale))
         for h in range(num_q_heads):
             g = kv_head_for_query_head(h, num_q_heads, num_kv_heads)
             out[i, h] = attend(q64[i, h], keys[:, g, :], values[:, g, :], sc)

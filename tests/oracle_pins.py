@@ -504,6 +504,73 @@ def pin_prefill_special_cases(o):
     assert np.array_equal(early, o.prefill(q[:10], kp, vp, bt[5:6], [10], [10], 0.3, "f32"))
 
 
+# ---------------------------------------------------------------------------
+# FP8 KV cache: OCP E4M3 codes with one float32 scale per pool
+# ---------------------------------------------------------------------------
+def pin_fp8_codec(o):
+    """Fixed values of the OFP8 E4M3 definition; every finite code survives
+    decode-encode; encoding is the nearest finite code with ties to an even
+    mantissa (found by brute force over all codes, not by the encoder's own
+    arithmetic), saturating at 448."""
+    dec = o.fp8_e4m3_decode
+    fixed = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0x77: 240.0, 0xB8: -1.0, 0xFE: -448.0}
+    for code, val in fixed.items():
+        assert dec(np.array([code], np.uint8))[0] == val
+    assert np.signbit(dec(np.array([0x80], np.uint8))[0])
+    assert np.isnan(dec(np.array([0x7F, 0xFF], np.uint8))).all()
+    codes = np.arange(256, dtype=np.uint8)
+    vals = dec(codes)
+    fin = ~np.isnan(vals)
+    assert np.array_equal(o.fp8_e4m3_encode(vals[fin].astype(np.float32)), codes[fin])
+    # brute force: nearest code, ties to even mantissa, on random values and
+    # on every midpoint between neighbouring codes
+    pos = np.sort(vals[:0x7F])                       # 0 .. 448, increasing
+    mids = (pos[1:] + pos[:-1]) / 2
+    rng = np.random.default_rng(5)
+    xs = np.concatenate([mids, -mids, rng.standard_normal(3000) * 40.0,
+                         np.exp2(rng.uniform(-12, 9, 3000)), [500.0, -1e6, 447.9, 2.0 ** -11]])
+    xs = xs.astype(np.float32)
+    got = o.fp8_e4m3_encode(xs)
+    for x, code in zip(xs.astype(np.float64), got):
+        a = min(abs(x), 448.0)
+        d = np.abs(pos - a)
+        best = np.flatnonzero(d == d.min())
+        k = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        want = k | (0x80 if np.signbit(x) else 0)
+        assert code == want, (x, code, want)
+
+
+def pin_fp8_decode(o):
+    """Decode over FP8 pools equals the plain decode over the dequantized
+    values (code times scale; scales of few significant bits keep that product
+    exact in float32), and the dequantized write is within half a step of the
+    original values."""
+    c = WINDOW_CASES[0]
+    q, kp, vp, bt, lens, ck, cv = _tiny_problem(c["seed"], c["lens"], c["Hq"], c["Hkv"],
+                                                c["D"], c["B"])
+    ks, vs = 3.0 / 64.0, 2.0 ** -5
+    kc = o.quantize_fp8(np.nan_to_num(kp), "f32", ks)
+    vc = o.quantize_fp8(np.nan_to_num(vp), "f32", vs)
+    got = o.decode(q, kc, vc, bt, lens, 0.3, "f32", kv_dtype="fp8e4m3", k_scale=ks, v_scale=vs)
+    kf = (o.fp8_e4m3_decode(kc) * np.float32(ks)).astype(np.float32)
+    vf = (o.fp8_e4m3_decode(vc) * np.float32(vs)).astype(np.float32)
+    assert np.array_equal(kf.astype(np.float64), o.fp8_e4m3_decode(kc) * float(np.float32(ks)))
+    want = o.decode(q, kf, vf, bt, lens, 0.3, "f32")
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-14)
+    x = np.random.default_rng(9).standard_normal(20000).astype(np.float32) * 3.0
+    err = np.abs(o.fp8_e4m3_decode(o.quantize_fp8(x, "f32", ks)) * np.float32(ks) - x)
+    step = np.where(np.abs(x) / ks < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.abs(x) / ks)) - 3)) * ks
+    assert (err <= step / 2 * (1 + 1e-6)).all()
+    # the slot write into FP8 pools stores the quantized rows at their slots
+    pool = np.zeros((4, 1, 2, 3), np.uint8)
+    k_new = np.array([[[1.0, -2.5, 1000.0]], [[0.1, 0.0, -0.3]]], np.float32)
+    kq, vq = o.write_kv_fp8(pool, pool, k_new, -k_new, [5, 0], 2, "f32", 0.5, 2.0)
+    assert np.array_equal(kq[2, 0, 1], o.quantize_fp8(k_new[0, 0], "f32", 0.5))
+    assert np.array_equal(vq[0, 0, 0], o.quantize_fp8(-k_new[1, 0], "f32", 2.0))
+    assert o.fp8_e4m3_decode(kq[2, 0, 1])[2] == 448.0      # 2000 saturates
+
+
 ALL_PINS = [
     pin_contiguous_bruteforce,
     pin_page_sketch_torch,
@@ -523,4 +590,6 @@ ALL_PINS = [
     pin_window_blocks,
     pin_prefill_bruteforce,
     pin_prefill_special_cases,
+    pin_fp8_codec,
+    pin_fp8_decode,
 ]

@@ -98,6 +98,28 @@ MUTANTS["window_ignored_in_gather"] = ("gather_window", _gather_window_all)
 MUTANTS["prefill_excludes_own_key"] = ("causal_keys", lambda p: int(p))
 MUTANTS["prefill_sees_next_key"] = ("causal_keys", lambda p: int(p) + 2)
 MUTANTS["prefill_rows_from_start"] = ("query_position", lambda T, M, r: int(r))
+def _fp8_truncating(y):
+    y = np.asarray(y, np.float32)
+    out = ref.__dict__["_orig_encode"](y)
+    a = np.abs(y.astype(np.float64))
+    dec = ref.fp8_e4m3_decode(out)
+    # round toward zero instead of to nearest
+    return np.where(np.abs(dec) > a, out - 1, out).astype(np.uint8)
+
+
+def _fp8_ties_up(y):
+    y = np.asarray(y, np.float32)
+    out = ref.__dict__["_orig_encode"](y)
+    a = np.abs(y.astype(np.float64))
+    up = ref.__dict__["_orig_encode"]((np.abs(y) * np.float32(1 + 2 ** -20)) * np.sign(y))
+    mid = np.abs(ref.fp8_e4m3_decode(out)) != np.abs(ref.fp8_e4m3_decode(up))
+    return np.where(mid & (a > 0), up, out).astype(np.uint8)
+
+
+MUTANTS["fp8_truncates"] = ("fp8_e4m3_encode", _fp8_truncating)
+MUTANTS["fp8_ties_away"] = ("fp8_e4m3_encode", _fp8_ties_up)
+MUTANTS["fp8_bias_8"] = ("fp8_e4m3_decode", lambda c: ref.__dict__["_orig_decode"](c) / 2.0)
+MUTANTS["fp8_scale_ignored"] = ("quantize_fp8", lambda x, d, s: ref.fp8_e4m3_encode(ref.to_float64(x, d).astype(np.float32)))
 MUTANTS["prefill_rows_shifted"] = ("query_position", lambda T, M, r: int(T) - int(M) + int(r) - 1)
 
 
@@ -117,6 +139,8 @@ def test_pins_catch_mutant(name, monkeypatch):
     attr, fn = MUTANTS[name]
     monkeypatch.setitem(ref.__dict__, "_orig_gather", ref.gather_tokens)
     monkeypatch.setitem(ref.__dict__, "_orig_write", ref.write_kv)
+    monkeypatch.setitem(ref.__dict__, "_orig_encode", ref.fp8_e4m3_encode)
+    monkeypatch.setitem(ref.__dict__, "_orig_decode", ref.fp8_e4m3_decode)
     monkeypatch.setattr(ref, attr, fn)
     failed = _run_pins()
     assert failed, f"no pin caught the planted mistake {name!r}"
