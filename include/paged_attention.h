@@ -171,6 +171,38 @@ pa_status pa_decode_sliding(const void* q, const void* k_pool, const void* v_poo
                             size_t workspace_bytes, int32_t partition_tokens, void* stream);
 
 /*
+ * FP8 KV pools ("vLLM Framework and Inference Engine Design", engine
+ * settings: kv_cache_dtype "fp8" halves the KV memory; "Inside vLLM"
+ * (besthub), "Quantization: Reducing Weight & KV Precision": the KV cache
+ * stored in FP8).  The pages fix neither format nor scale; here the pools
+ * hold OCP E4M3 codes (1 byte per element, same [num_blocks][num_kv_heads]
+ * [block_size][head_dim] layout) with one float32 scale for the key pool and
+ * one for the value pool: code = E4M3(x / scale), rounded to nearest even and
+ * saturated to +-448; value = code * scale.  pool->dtype names the element
+ * type of the rows written (k, v) and of q and out.
+ *
+ * pa_write_kv_fp8 -- pa_write_kv into FP8 pools: k and v ([num_tokens]
+ *                 [num_kv_heads][head_dim], pool->dtype, any of the three)
+ *                 are quantized with k_scale / v_scale (finite, > 0).
+ * pa_decode_fp8 -- pa_decode over FP8 pools (q and out fp16 or bf16).  The
+ *                 codes are converted exactly to the compute type; the key
+ *                 scale multiplies the scores and the value scale the output.
+ *                 Always the balanced split: partition_tokens is 0 and fp32,
+ *                 blocks under 16 tokens or over 1024 sequences return
+ *                 PA_ERR_UNSUPPORTED.  Workspace: pa_decode_workspace_bytes
+ *                 with the same desc and partition_tokens 0.
+ */
+pa_status pa_write_kv_fp8(const void* k, const void* v, const int32_t* slot_mapping,
+                          int32_t num_tokens, void* k_pool, void* v_pool,
+                          const pa_pool_desc* pool, float k_scale, float v_scale, void* stream);
+pa_status pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                        const pa_pool_desc* pool, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_q_heads, float scale, float k_scale,
+                        float v_scale, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * pa_append_decode -- one whole decode step in one call: every sequence's
  * newest token is placed in the pools and then attended over, with the same
  * result as

@@ -72,6 +72,10 @@ def lib():
                               ctypes.c_float, vp, vp, sz, i32, vp], c_int),
         "pa_prefill": ([vp, vp, vp, desc, vp, i32, vp, vp, i32, i32, i32, i32, ctypes.c_float,
                         vp, vp], c_int),
+        "pa_write_kv_fp8": ([vp, vp, vp, i32, vp, vp, desc, ctypes.c_float, ctypes.c_float, vp],
+                            c_int),
+        "pa_decode_fp8": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                           ctypes.c_float, ctypes.c_float, vp, vp, sz, vp], c_int),
         "pa_profile_start": ([], c_int),
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
@@ -131,6 +135,16 @@ def pool_desc(k_pool) -> pa_pool_desc:
     return pa_pool_desc(nb, bs, hkv, d, dtype_code(k_pool))
 
 
+def fp8_pool_desc(k_pool, element) -> pa_pool_desc:
+    """Descriptor of an FP8 pool (uint8 codes, [NB][Hkv][B][D]) whose rows are
+    written from, and read into, tensors of ``element``'s dtype."""
+    torch = _torch()
+    if k_pool.dim() != 4 or k_pool.dtype != torch.uint8:
+        raise ValueError("FP8 pools are uint8 [num_blocks][num_kv_heads][block_size][head_dim]")
+    nb, hkv, bs, d = (int(x) for x in k_pool.shape)
+    return pa_pool_desc(nb, bs, hkv, d, dtype_code(element))
+
+
 def _stream(stream):
     if stream is not None:
         return int(stream) if not hasattr(stream, "cuda_stream") else int(stream.cuda_stream)
@@ -168,6 +182,68 @@ def pa_write_kv(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
                            _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_write_kv")
+
+
+def pa_write_kv_fp8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale, stream=None) -> None:
+    """pa_write_kv into FP8 (E4M3) pools: each row of k, v is stored as
+    codes of x / scale."""
+    torch = _torch()
+    desc = fp8_pool_desc(k_pool, k)
+    dev = k_pool.device
+    for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
+        _check(t, n, dtype=torch.uint8, device=dev)
+    for t, n in ((k, "k"), (v, "v")):
+        _check(t, n, dtype=k.dtype, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(slot_mapping, "slot_mapping", dtype=torch.int32, dim=1, device=dev)
+    n_tok = int(slot_mapping.shape[0])
+    want = (n_tok, desc.num_kv_heads, desc.head_dim)
+    if tuple(k.shape) != want or tuple(v.shape) != want:
+        raise ValueError(f"k and v must be {want}")
+    st = lib().pa_write_kv_fp8(k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), n_tok,
+                               k_pool.data_ptr(), v_pool.data_ptr(), ctypes.byref(desc),
+                               float(k_scale), float(v_scale), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_write_kv_fp8")
+
+
+def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale,
+                  out=None, max_context_len=None, workspace=None, stream=None):
+    """pa_decode over FP8 (E4M3) pools with per-pool scales."""
+    torch = _torch()
+    desc = fp8_pool_desc(k_pool, q)
+    dev = k_pool.device
+    _check(k_pool, "k_pool", dtype=torch.uint8, device=dev)
+    _check(v_pool, "v_pool", dtype=torch.uint8, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(q, "q", dim=3, device=dev)
+    _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    n, hq, d = (int(x) for x in q.shape)
+    if d != desc.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if n else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, device=dev)
+    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, 0)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", device=dev)
+    st = lib().pa_decode_fp8(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                             ctypes.byref(desc), block_tables.data_ptr(),
+                             int(block_tables.shape[1]), context_lens.data_ptr(), n,
+                             int(max_context_len), hq, float(scale), float(k_scale),
+                             float(v_scale), out.data_ptr(), workspace.data_ptr(),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_fp8")
+    return out
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, desc: pa_pool_desc,

@@ -52,7 +52,8 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
                  int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
                  int32_t max_context_len, int32_t num_q_heads, float scale, void* out,
                  void* workspace, size_t workspace_bytes, int32_t partition_tokens,
-                 int32_t window, void* stream) {
+                 int32_t window, void* stream, bool kv_fp8 = false, float k_scale = 1.0f,
+                 float v_scale = 1.0f) {
   pa::DecodePlan plan;
   pa_status s = pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len,
                                 max_blocks_per_seq, partition_tokens, &plan);
@@ -68,7 +69,14 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
     if (reinterpret_cast<uintptr_t>(workspace) % 16 != 0) return PA_ERR_INVALID_ARGUMENT;
   }
 
-  pa::DecodeArgs a;
+  if (kv_fp8) {
+    // FP8 pools: the balanced split with 16-bit queries only
+    if (!plan.balanced || pool->dtype == PA_F32) return PA_ERR_UNSUPPORTED;
+    if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+      return PA_ERR_INVALID_ARGUMENT;
+  }
+
+  pa::DecodeArgs a{};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -89,7 +97,11 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
   a.partition_tokens = plan.partition_tokens;
   a.num_partitions = plan.balanced ? 0 : plan.num_partitions;
   a.min_split_tiles = pa::kMinSplitTiles;
-  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * 1.4426950408889634);
+  // FP8 pools: scores are taken on the codes, so the key scale joins the scale
+  a.scale_log2 = static_cast<float>(static_cast<double>(scale) * (kv_fp8 ? k_scale : 1.0f) *
+                                    1.4426950408889634);
+  a.kv_fp8 = kv_fp8 ? 1 : 0;
+  a.v_scale = kv_fp8 ? v_scale : 1.0f;
   a.new_k = new_k;
   a.new_v = new_v;
   a.window = window;
@@ -123,6 +135,44 @@ pa_status pa_decode_sliding(const void* q, const void* k_pool, const void* v_poo
   return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                 context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
                 workspace_bytes, partition_tokens, window, stream);
+}
+
+pa_status pa_write_kv_fp8(const void* k, const void* v, const int32_t* slot_mapping,
+                          int32_t num_tokens, void* k_pool, void* v_pool,
+                          const pa_pool_desc* pool, float k_scale, float v_scale, void* stream) {
+  const pa_status s = pa::check_write(k, v, slot_mapping, num_tokens, k_pool, v_pool, pool);
+  if (s != PA_OK) return s;
+  if (!(std::isfinite(k_scale) && k_scale > 0.0f && std::isfinite(v_scale) && v_scale > 0.0f))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens == 0) return PA_OK;
+  pa::WriteArgs a;
+  a.k = k;
+  a.v = v;
+  a.slot_mapping = slot_mapping;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.num_tokens = num_tokens;
+  a.num_slots = pool->num_blocks * pool->block_size;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.row_bytes = pool->head_dim;                 // one byte per code
+  int32_t lb = 0;
+  while ((1 << lb) < pool->block_size) ++lb;
+  a.log2_block = lb;
+  return pa::launch_write_kv_fp8(a, pool->dtype, k_scale, v_scale,
+                                 static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
+}
+
+pa_status pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
+                        const pa_pool_desc* pool, const int32_t* block_tables,
+                        int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t num_seqs,
+                        int32_t max_context_len, int32_t num_q_heads, float scale, float k_scale,
+                        float v_scale, void* out, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                workspace_bytes, 0, 0, stream, true, k_scale, v_scale);
 }
 
 pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,

@@ -60,9 +60,18 @@ struct DecodeArgs {
   // out) are sequence i's queries, the last M_i of its T_i tokens.
   const int32_t* query_start;
   int32_t max_query_len;    // host bound on M_i (sizes the grid)
+  // FP8 pools (balanced split only): codes times v_scale are the values; the
+  // key scale is folded into scale_log2
+  int32_t kv_fp8;
+  float v_scale;
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
+
+// Slot write into FP8 (E4M3) pools; a.row_bytes = head_dim (one byte per
+// code); dtype = element type of k and v.
+hipError_t launch_write_kv_fp8(const WriteArgs& a, int32_t dtype, float k_scale, float v_scale,
+                               hipStream_t stream);
 
 // Chunked prefill (16-bit pools): causal attention of each sequence's last
 // M_i tokens; group as planned.

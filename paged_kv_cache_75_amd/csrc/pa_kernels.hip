@@ -206,6 +206,69 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   }
 }
 
+// FP8 pools: E4M3 code of a float32 value y = x / scale, rounded to nearest
+// with ties to an even mantissa; 448 and above (infinities too) saturate to
+// 448, NaN stays NaN.  Written from the OCP 8-bit floating point definition:
+// 4 exponent bits with bias 7, 3 mantissa bits, S.1111.111 reserved for NaN.
+__device__ inline uint32_t e4m3_code(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80;
+  const uint32_t mag = u & 0x7fffffff;
+  if (mag > 0x7f800000) return sign | 0x7f;                  // NaN
+  const float a = __uint_as_float(mag);
+  if (a >= 448.0f) return sign | 0x7e;
+  if (a < 0.015625f)                                          // below 2^-6: multiples of 2^-9
+    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // exact scaling, RNE
+  uint32_t E = (mag >> 23) - 120;                             // (e - 127) + 7, in 1 .. 15
+  uint32_t m = (mag >> 20) & 7;
+  const uint32_t rest = mag & 0xfffff;                        // the 20 bits below m
+  if (rest > 0x80000 || (rest == 0x80000 && (m & 1))) ++m;
+  if (m == 8) {
+    m = 0;
+    ++E;
+  }
+  return sign | (E << 3) | m;                                 // a < 448 keeps this finite
+}
+
+// Slot write into FP8 pools: one workgroup per new token, four elements per
+// thread (one 32-bit store of codes).
+template <int DT>
+__global__ __launch_bounds__(256) void write_kv_fp8_kernel(WriteArgs a, float k_scale,
+                                                          float v_scale) {
+  const int n = blockIdx.x;
+  const int32_t slot = a.slot_mapping[n];
+  if (slot < 0 || slot >= a.num_slots) return;
+  const int64_t blk = slot >> a.log2_block;
+  const int64_t off = slot & ((1 << a.log2_block) - 1);
+  const int D = a.row_bytes;                     // FP8 pools: row bytes = head_dim
+  const int quads = a.num_kv_heads * D / 4;
+  for (int c = threadIdx.x; c < 2 * quads; c += blockDim.x) {
+    const bool is_v = c >= quads;
+    const int cc = is_v ? c - quads : c;
+    const int h = cc / (D / 4);
+    const int e0 = (cc - h * (D / 4)) * 4;
+    const int64_t src = (int64_t(n) * a.num_kv_heads + h) * D + e0;
+    const void* x = is_v ? a.v : a.k;
+    const float scale = is_v ? v_scale : k_scale;
+    uint32_t word = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float f;
+      if constexpr (DT == PA_F32) {
+        f = static_cast<const float*>(x)[src + e];
+      } else if constexpr (DT == PA_F16) {
+        f = static_cast<float>(static_cast<const _Float16*>(x)[src + e]);
+      } else {
+        f = __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[src + e]) << 16);
+      }
+      word |= e4m3_code(f / scale) << (8 * e);
+    }
+    char* dst = static_cast<char*>(is_v ? a.v_pool : a.k_pool) +
+                ((blk * a.num_kv_heads + h) << a.log2_block | off) * D + e0;
+    *reinterpret_cast<uint32_t*>(dst) = word;
+  }
+}
+
 // Appending decode: copy row (i, h) of new_k / new_v to token T_i - 1 of
 // sequence i, through its block table (lengths clamped as in the decode).
 // Sequences with no tokens and table entries outside the pool are skipped.
@@ -341,6 +404,25 @@ template <> __device__ inline v4i16 pack4<PA_F16>(const float* p) {
   return __builtin_bit_cast(v4i16, x);
 }
 
+// FP8 (OCP E4M3) codes to the compute type, exactly: the gfx950 conversion
+// instruction turns the two codes in the low 16 bits of a word into two
+// bf16 / fp16 values (checked against the E4M3 definition for all 256 codes).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+template <int DT> __device__ inline uint32_t fp8x2_to(uint32_t w);
+template <> __device__ inline uint32_t fp8x2_to<PA_BF16>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false));
+}
+template <> __device__ inline uint32_t fp8x2_to<PA_F16>(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false));
+}
+// codes 8h .. 8h+7 of a 16-code chunk as eight 16-bit values (one MFMA chunk)
+template <int DT> __device__ inline uint4 fp8x8_to(const uint4& c, int h) {
+  const uint32_t w0 = h ? c.z : c.x, w1 = h ? c.w : c.y;
+  return make_uint4(fp8x2_to<DT>(w0), fp8x2_to<DT>(w0 >> 16), fp8x2_to<DT>(w1),
+                    fp8x2_to<DT>(w1 >> 16));
+}
+
 template <int DT, int D, int G>
 struct MfmaPv {
   using GE = Geo<DT, D, G>;
@@ -390,6 +472,18 @@ struct MfmaPv {
     const uint4* qrow = reinterpret_cast<const uint4*>(qs + head * kRowBytes);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) qb[kk] = c < G ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+  }
+
+  // FP8 pools: key chunk kk of a lane holds elements 16 (gq + 4 kk) .. +16,
+  // converted to two MFMA chunks (h = 0, 1); the query chunks follow suit
+  __device__ __forceinline__ void load_q_lds_fp8(const char* qs) {
+    const int head = c < G ? c : 0;
+    const uint4* qrow = reinterpret_cast<const uint4*>(qs + head * kRowBytes);
+#pragma unroll
+    for (int kk = 0; kk < KK / 2; ++kk)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+        qb[2 * kk + h] = c < G ? qrow[2 * (gq + 4 * kk) + h] : make_uint4(0, 0, 0, 0);
   }
 
   float p_[4];
@@ -457,12 +551,14 @@ struct MfmaPv {
   // One wave holds the whole segment: write its result from registers.
   // complete: out rows (row0 + c) get O/l; otherwise the piece slot gets
   // O/l, the running max and the sum.  Lane (gq, c < G) owns d = 16n+4gq+i.
-  __device__ __forceinline__ void store_result(const DecodeArgs& a, int64_t row0, bool complete, int piece) {
+  // out_scale multiplies the result (the value scale of FP8 pools; 1 otherwise)
+  __device__ __forceinline__ void store_result(const DecodeArgs& a, int64_t row0, bool complete,
+                                               int piece, float out_scale = 1.0f) {
     float l = l_run;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     if (c >= G) return;
-    const float inv = 1.0f / l;
+    const float inv = (1.0f / l) * out_scale;
     if (complete) {
 #pragma unroll
       for (int n = 0; n < NT; ++n) store4<DT>(a.out, (row0 + c) * D + 16 * n + 4 * gq, o[n] * inv);
@@ -863,12 +959,18 @@ struct StreamSmem {
   int64_t new_dst[kAppend ? kSegCap : 1];   // pool byte offset of the new row, or -1
 };
 
-template <int DT, int D, int G, bool kAppend, bool kWindow>
+template <int DT, int D, int G, bool kAppend, bool kWindow, bool kFp8>
 __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, G>;
   using SM = StreamSmem<DT, D, G, kAppend>;
   const int window = kWindow ? a.window : 0;      // 0: every token
-  constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
+  // pool rows: D codes (FP8 pools) or D elements of DT; the query rows, the LDS
+  // value tile and the tile math always use DT
+  constexpr int kPoolRowBytes = kFp8 ? D : GE::kRowBytes;
+  constexpr int CPR = kPoolRowBytes / 16;         // 16-byte chunks per pool row
+  constexpr int KK = CPR / 4;                     // key chunks per lane per tile
+  constexpr int RPI = kWave / CPR;                // value rows per load instruction
+  constexpr int VS = kTileTokens / RPI;           // value loads per lane per tile
   constexpr int kRowBytes = GE::kRowBytes;
   __shared__ SM sm;
 
@@ -929,8 +1031,8 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   MfmaPv<DT, D, G> tm;
   tm.set_lane(lane);
   const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
-  const int k_off = c * kRowBytes + gq * 16;          // key chunk gq of row c; +64 per kk
-  const int v_off = rho * kRowBytes + chi * 16;       // value chunk chi of row rho
+  const int k_off = c * kPoolRowBytes + gq * 16;      // key chunk gq of row c; +64 per kk
+  const int v_off = rho * kPoolRowBytes + chi * 16;   // value chunk chi of row rho
   const int64_t blk_rows = int64_t(Hkv) << lb;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
@@ -1019,7 +1121,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
       const int32_t entry = table[t0 >> lb];
       const int64_t blk = min(max(entry, 0), a.num_blocks - 1);
-      doff = (blk * blk_rows + (int64_t(sm.seg_g[sg]) << lb) + (t0 & bmask)) * kRowBytes;
+      doff = (blk * blk_rows + (int64_t(sm.seg_g[sg]) << lb) + (t0 & bmask)) * kPoolRowBytes;
       const int live = min(kTileTokens, T - t0);
       // the sequence's newest token is in this tile and comes from new_k/new_v
       const bool app = kAppend && t0 + live == T;
@@ -1038,7 +1140,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     // spans the live rows only, so rows past a sequence's end load as zeros
     auto rsrc = [&](const char* base, int64_t off, int live) {
       return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0,
-                                               live * kRowBytes, kBufferDword3);
+                                               live * kPoolRowBytes, kBufferDword3);
     };
     struct Keys {
       KeyRegs<DT, D> r;
@@ -1068,7 +1170,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < VS; ++s2)
         vr.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rv, v_off + s2 * RPI * kRowBytes, 0, 0));
+                                                 rv, v_off + s2 * RPI * kPoolRowBytes, 0, 0));
     };
     // Appending tile: the newest row of the keys and of the values comes from
     // the segment's LDS copy of new_k / new_v (register selects only, so the
@@ -1106,15 +1208,41 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       if (sg != cur) {               // a new segment begins
         cur = sg;
         tm.reset();
-        tm.load_q_lds(sm.q[sg]);
+        if constexpr (kFp8)
+          tm.load_q_lds_fp8(sm.q[sg]);
+        else
+          tm.load_q_lds(sm.q[sg]);
       }
       if constexpr (kAppend)
         if (kr.meta & kMetaAppend) put_new_row(kr);
       const int first = kWindow ? (kr.meta >> 12) & 0xf : 0;
       if (kWindow && first > 0) clear_rows_below(vr, first, rho);
-      tm.stage_values(vr, sm.vtile);
+      if constexpr (kFp8) {
+        // each chunk of 16 value codes becomes two 16-bit chunks of the row
+#pragma unroll
+        for (int s2 = 0; s2 < VS; ++s2) {
+          const int row = s2 * RPI + rho;
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            *reinterpret_cast<uint4*>(sm.vtile + row * kRowBytes +
+                                      (((2 * chi + h) ^ MfmaPv<DT, D, G>::swz(row)) << 4)) =
+                fp8x8_to<DT>(vr.v[s2], h);
+        }
+      } else {
+        tm.stage_values(vr, sm.vtile);
+      }
       if (k + 1 < ntot) load_vals(k + 1);
-      tm.scores(a, kr.r, first, kr.meta & kMetaLive);
+      if constexpr (kFp8) {
+        KeyRegs<DT, D> kb;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          kb.k[2 * kk] = fp8x8_to<DT>(kr.r.k[kk], 0);
+          kb.k[2 * kk + 1] = fp8x8_to<DT>(kr.r.k[kk], 1);
+        }
+        tm.scores(a, kb, first, kr.meta & kMetaLive);
+      } else {
+        tm.scores(a, kr.r, first, kr.meta & kMetaLive);
+      }
       if (k + 2 < ntot) load_keys(k + 2, kr);
       tm.accumulate(sm.vtile);
       if (k + 1 == sm.seg_start[sg] + sm.seg_n[sg]) {   // the segment's last tile
@@ -1123,7 +1251,8 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
         const int piece = 2 * w + ((flags & 4) ? 1 : 0);
         const int seq = sm.seg_seq[sg];
         const int g = sm.seg_g[sg];
-        tm.store_result(a, int64_t(seq) * Hq + int64_t(g) * G, complete, piece);
+        tm.store_result(a, int64_t(seq) * Hq + int64_t(g) * G, complete, piece,
+                        kFp8 ? a.v_scale : 1.0f);
         if (!complete && lane == 0) {
           int32_t* hdr = a.ws_hdr + piece * kHdrInts;
           hdr[1] = seq;
@@ -1563,22 +1692,26 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
     if constexpr (DT == PA_F32) {
       return hipErrorInvalidValue;
     } else {
-      // variants: appending decode, sliding window, plain (never both of the first two)
-      const int mode = a.new_k != nullptr ? 1 : a.window > 0 ? 2 : 0;
+      // variants: appending decode, sliding window, FP8 pools, plain (one at a time)
+      const int mode = a.new_k != nullptr ? 1 : a.window > 0 ? 2 : a.kv_fp8 ? 3 : 0;
       const void* k =
-          mode == 1 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true, false>)
-          : mode == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, true>)
-                      : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false>);
+          mode == 1 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true, false, false>)
+          : mode == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, true, false>)
+          : mode == 3 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, true>)
+                      : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, false>);
       const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 4 + mode, kWave);
       if (W <= 0) return hipErrorInvalidDevice;
       if (mode == 1)
-        launch_attention(decode_stream_kernel<DT, D, G, true, false>, dim3(W), dim3(kWave),
+        launch_attention(decode_stream_kernel<DT, D, G, true, false, false>, dim3(W), dim3(kWave),
                          stream, a);
       else if (mode == 2)
-        launch_attention(decode_stream_kernel<DT, D, G, false, true>, dim3(W), dim3(kWave),
+        launch_attention(decode_stream_kernel<DT, D, G, false, true, false>, dim3(W), dim3(kWave),
+                         stream, a);
+      else if (mode == 3)
+        launch_attention(decode_stream_kernel<DT, D, G, false, false, true>, dim3(W), dim3(kWave),
                          stream, a);
       else
-        launch_attention(decode_stream_kernel<DT, D, G, false, false>, dim3(W), dim3(kWave),
+        launch_attention(decode_stream_kernel<DT, D, G, false, false, false>, dim3(W), dim3(kWave),
                          stream, a);
       hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W),
                          dim3(MergeShape<G, D>::kThreads), 0, stream, a, W);
@@ -1728,6 +1861,28 @@ hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   hipLaunchKernelGGL(write_kv_kernel, dim3(a.num_tokens), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_kv_fp8(const WriteArgs& a, int32_t dtype, float k_scale, float v_scale,
+                               hipStream_t stream) {
+  if (a.num_tokens == 0) return hipSuccess;
+  switch (dtype) {
+    case PA_F32:
+      hipLaunchKernelGGL(write_kv_fp8_kernel<PA_F32>, dim3(a.num_tokens), dim3(256), 0, stream, a,
+                         k_scale, v_scale);
+      break;
+    case PA_F16:
+      hipLaunchKernelGGL(write_kv_fp8_kernel<PA_F16>, dim3(a.num_tokens), dim3(256), 0, stream, a,
+                         k_scale, v_scale);
+      break;
+    case PA_BF16:
+      hipLaunchKernelGGL(write_kv_fp8_kernel<PA_BF16>, dim3(a.num_tokens), dim3(256), 0, stream,
+                         a, k_scale, v_scale);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

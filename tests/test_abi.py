@@ -14,6 +14,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so
 def test_exports_every_declared_function():
     names = B.declared_functions()
     assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding", "pa_prefill",
+            "pa_write_kv_fp8", "pa_decode_fp8",
             "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
             "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
@@ -186,3 +187,27 @@ def prefill(d, **kw):
 ])
 def test_prefill_validation(kw, dt, want):
     assert prefill(desc(dt=dt), **kw) == want
+
+
+@pytest.mark.parametrize("ks,vs,dt,bs,n,want", [
+    (0.0, 0.1, B.PA_BF16, 16, 4, B.PA_ERR_INVALID_ARGUMENT),       # scales must be > 0
+    (0.1, float("nan"), B.PA_BF16, 16, 4, B.PA_ERR_INVALID_ARGUMENT),
+    (0.1, 0.1, B.PA_F32, 16, 4, B.PA_ERR_UNSUPPORTED),             # 16-bit queries only
+    (0.1, 0.1, B.PA_BF16, 8, 4, B.PA_ERR_UNSUPPORTED),             # balanced split only
+    (0.1, 0.1, B.PA_BF16, 16, 2000, B.PA_ERR_UNSUPPORTED),
+    (0.1, 0.1, B.PA_F16, 16, 0, B.PA_OK),
+])
+def test_decode_fp8_validation(ks, vs, dt, bs, n, want):
+    d = desc(bs=bs, dt=dt)
+    got = B.lib().pa_decode_fp8(FAKE, FAKE, FAKE, ctypes.byref(d), FAKE, 16, FAKE, n, 100, 8, 0.1,
+                                ks, vs, FAKE, FAKE, 1 << 26, None)
+    assert got == want
+
+
+@pytest.mark.parametrize("ks,vs,want", [(0.0, 1.0, B.PA_ERR_INVALID_ARGUMENT),
+                                        (1.0, -2.0, B.PA_ERR_INVALID_ARGUMENT),
+                                        (1.0, float("inf"), B.PA_ERR_INVALID_ARGUMENT)])
+def test_write_kv_fp8_validation(ks, vs, want):
+    d = desc()
+    assert B.lib().pa_write_kv_fp8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), ks, vs,
+                                   None) == want

@@ -479,3 +479,74 @@ def test_prefill_full_size():
     w = workloads.make(3, seed=2000, num_seqs=16)
     mq = [min(512, int(T)) for T in w.context_lens]
     _prefill_case(w, mq, 2001, "llama3-8b prefill", sample_rows=[0, 5, 10, 15])
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) pools: pa_write_kv_fp8 bit-exact, pa_decode_fp8 against the oracle
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "f16", "bf16"])
+def test_write_kv_fp8_codes(dtype):
+    """Codes written for rows spanning the saturated, normal and subnormal
+    ranges (and -0, NaN) equal the oracle's quantization bit for bit."""
+    import torch
+    from workloads.generate import round_to_dtype
+    from paged_kv_cache_75_amd import pa_write_kv_fp8
+    rng = np.random.default_rng(2100)
+    NB, H, B, D, n = 12, 2, 16, 128, 40
+    mags = np.exp2(rng.uniform(-16, 12, (n, H, D))) * rng.choice([-1.0, 1.0], (n, H, D))
+    x = mags.astype(np.float32)
+    x[0, 0, :4] = [0.0, -0.0, np.inf, -np.inf]
+    x[0, 0, 4] = np.nan
+    x[1, 0, :3] = [448.0 * 0.05, 464.0 * 0.05, 2.0 ** -10 * 0.05]   # ties and the saturation edge
+    k = round_to_dtype(x, dtype)
+    v = round_to_dtype(-x * 3.0, dtype)
+    slots = rng.permutation(NB * B)[:n].astype(np.int32)
+    slots[3] = -1                                    # skipped
+    pool0 = rng.integers(0, 256, (NB, H, B, D), dtype=np.uint8)
+    kp = torch.from_numpy(pool0.copy()).to(DEV)
+    vp = torch.from_numpy(pool0.copy()).to(DEV)
+    from gpu_util import to_device
+    pa_write_kv_fp8(to_device(k, dtype, DEV), to_device(v, dtype, DEV), to_device(slots, None, DEV),
+                    kp, vp, 0.05, 0.75)
+    _sync()
+    want_k, want_v = ref.write_kv_fp8(pool0, pool0, k, v, slots, B, dtype, 0.05, 0.75)
+    assert np.array_equal(kp.cpu().numpy(), want_k)
+    assert np.array_equal(vp.cpu().numpy(), want_v)
+
+
+def _fp8_case(w, k_scale, v_scale, label, seqs=None):
+    import torch
+    from paged_kv_cache_75_amd import pa_decode_fp8, pa_write_kv_fp8
+    dw = upload(w, DEV)
+    kc = ref.quantize_fp8(w.k_pool, w.dtype, k_scale)
+    vc = ref.quantize_fp8(w.v_pool, w.dtype, v_scale)
+    kp, vp = torch.from_numpy(kc).to(DEV), torch.from_numpy(vc).to(DEV)
+    say(f"[fp8] {label}: write + decode")
+    pa_write_kv_fp8(dw.new_k, dw.new_v, dw.slot_mapping, kp, vp, k_scale, v_scale)
+    out = pa_decode_fp8(dw.q, kp, vp, dw.block_tables, dw.context_lens, dw.scale, k_scale, v_scale,
+                        max_context_len=dw.max_context_len)
+    _sync()
+    kq, vq = ref.write_kv_fp8(kc, vc, w.new_k, w.new_v, w.slot_mapping, w.block_size, w.dtype,
+                              k_scale, v_scale, inplace=True)
+    assert np.array_equal(kp.cpu().numpy(), kq) and np.array_equal(vp.cpu().numpy(), vq)
+    want = ref.decode(w.q, kq, vq, w.block_tables, w.context_lens, w.scale, w.dtype, seqs=seqs,
+                      kv_dtype="fp8e4m3", k_scale=k_scale, v_scale=v_scale)
+    compare(to_f64(out), want, w.dtype, seqs=seqs, label=label)
+
+
+@pytest.mark.parametrize("cfg", [3, 2, 5])
+def test_decode_fp8_configs(cfg):
+    """FP8 pools (scales mapping about +-4 to the top of the range) for the
+    Llama-3-8B, Qwen2-0.5B and prefix-shared batches."""
+    w = workloads.make(cfg, seed=2200 + cfg)
+    _fp8_case(w, 4.0 / 448.0, 5.0 / 448.0, f"config {cfg} fp8")
+
+
+def test_decode_fp8_edges():
+    """Short and empty sequences, ragged tails, G = 16."""
+    lens = [1, 2, 15, 16, 17, 0, 33, 100, 257]
+    w = workloads.random_paged("fp8-edges", "bf16", 32, 2, 128, 16, lens, seed=2300,
+                               spare_frac=0.1)
+    _fp8_case(w, 0.01, 0.02, "fp8 edges G=16")
+    w = workloads.random_paged("fp8-edges64", "f16", 8, 4, 64, 32, lens, seed=2301)
+    _fp8_case(w, 0.03, 0.005, "fp8 edges f16 D=64 B=32")
