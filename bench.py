@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0,
                     help="chunked prefill instead of decode: every sequence of the first 16 of "
                          "the Llama-3-8B batch gets a chunk of this many new tokens (pa_prefill)")
+    ap.add_argument("--fp8", action="store_true",
+                    help="FP8 (E4M3) pools with per-pool scales: pa_write_kv_fp8 + pa_decode_fp8")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
@@ -80,7 +82,7 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float, window: int = 0):
+def cpu_baseline(w, budget_s: float, window: int = 0, fp8_scales=None):
     """The oracle as it stands (write, then decode), on the same host arrays,
     one BLAS thread; repeated over growing sequence samples until the budget
     is spent.  Returns TB/s of KV bytes read, the sample description, cores."""
@@ -90,14 +92,25 @@ def cpu_baseline(w, budget_s: float, window: int = 0):
     from threadpoolctl import threadpool_limits
     bytes_done, secs, reps = 0, 0.0, 0
     n = w.num_seqs
+    if fp8_scales:
+        kc = ref.quantize_fp8(w.k_pool, w.dtype, fp8_scales[0])
+        vc = ref.quantize_fp8(w.v_pool, w.dtype, fp8_scales[1])
     with threadpool_limits(1):
         while secs < budget_s and reps < 100:
             t0 = time.perf_counter()
-            k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size)
-            ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
-                       seqs=np.arange(n), window=window or None)
+            if fp8_scales:
+                k, v = ref.write_kv_fp8(kc, vc, w.new_k, w.new_v, w.slot_mapping, w.block_size,
+                                        w.dtype, *fp8_scales)
+                ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
+                           seqs=np.arange(n), kv_dtype="fp8e4m3", k_scale=fp8_scales[0],
+                           v_scale=fp8_scales[1])
+            else:
+                k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping,
+                                    w.block_size)
+                ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
+                           seqs=np.arange(n), window=window or None)
             secs += time.perf_counter() - t0
-            bytes_done += kv_bytes_per_step(w, window)
+            bytes_done += kv_bytes_per_step(w, window) // (w.elem_bytes if fp8_scales else 1)
             reps += 1
     sample = f"{reps} full steps of the same batch (write + decode, all {n} seqs), {secs:.1f} s"
     return bytes_done / secs / 1e12, sample, 1
@@ -248,9 +261,10 @@ def main():
     import torch
 
     import workloads
-    from paged_kv_cache_75_amd import (pa_append_decode, pa_decode, pa_decode_sliding,
+    from paged_kv_cache_75_amd import (fp8_pool_desc, pa_append_decode, pa_decode,
+                                       pa_decode_fp8, pa_decode_sliding,
                                        pa_decode_workspace_bytes, pa_profile_start,
-                                       pa_profile_stop, pa_write_kv, pool_desc)
+                                       pa_profile_stop, pa_write_kv, pa_write_kv_fp8, pool_desc)
 
     if not torch.cuda.is_available():
         sys.exit("bench.py needs a GPU")
@@ -275,18 +289,33 @@ def main():
     slots = up(w.slot_mapping.astype(np.int32), None)
     nk, nv = up(w.new_k, w.dtype), up(w.new_v, w.dtype)
     k0, v0 = up(w.k_pool, w.dtype), up(w.v_pool, w.dtype)
+    ks = vs = 4.0 / 448.0              # FP8 pools: about +-4 maps to the top of E4M3
+    if args.fp8:
+        # every slot of the pools quantized on the GPU by the slot write
+        nb, hkv, bsz, hd = (int(x) for x in k0.shape)
+        allslots = torch.arange(nb * bsz, dtype=torch.int32, device=dev)
+        kq = torch.empty(k0.shape, dtype=torch.uint8, device=dev)
+        vq = torch.empty_like(kq)
+        pa_write_kv_fp8(k0.permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous(),
+                        v0.permute(0, 2, 1, 3).reshape(-1, hkv, hd).contiguous(), allslots,
+                        kq, vq, ks, vs)
+        torch.cuda.synchronize()
+        k0, v0 = kq, vq
     pool_bytes = 2 * k0.numel() * k0.element_size()
     reps = args.replicas or max(1, min(8, -(-(1 << 30) // pool_bytes) + 1))
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
     out = torch.empty_like(q)
-    desc = pool_desc(k0)
+    desc = fp8_pool_desc(k0, q) if args.fp8 else pool_desc(k0)
     ws_bytes = pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, desc, w.max_context_len,
                                          args.partition)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     writes = cfg in (3, 5)
 
     def decode(kp, vp):
-        if args.window:
+        if args.fp8:
+            pa_decode_fp8(q, kp, vp, bt, cl, w.scale, ks, vs, out=out,
+                          max_context_len=w.max_context_len, workspace=ws)
+        elif args.window:
             pa_decode_sliding(q, kp, vp, bt, cl, w.scale, args.window, out=out,
                               max_context_len=w.max_context_len, workspace=ws,
                               partition_tokens=args.partition)
@@ -339,13 +368,16 @@ def main():
         return (t1 - t0) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in ev], kernel_us
 
     def write(kp, vp):
-        pa_write_kv(nk, nv, slots, kp, vp)
+        if args.fp8:
+            pa_write_kv_fp8(nk, nv, slots, kp, vp, ks, vs)
+        else:
+            pa_write_kv(nk, nv, slots, kp, vp)
 
     def nothing(kp, vp):
         pass
 
     K = args.steps
-    fused = writes and args.step != "two-call" and not args.window
+    fused = writes and args.step != "two-call" and not args.window and not args.fp8
     two_call = writes and args.step != "append"
     if two_call:
         two_ms, two_decode_ms, two_kernel_us = timed(write, decode)
@@ -356,7 +388,7 @@ def main():
     else:
         ms_per_step, decode_ms, kernel_us = timed(nothing, decode)
 
-    kv_bytes = kv_bytes_per_step(w, args.window)
+    kv_bytes = kv_bytes_per_step(w, args.window) // (w.elem_bytes if args.fp8 else 1)
     balanced = args.partition == 0 and w.dtype != "f32" and w.block_size >= 16 and w.num_seqs <= 1024
     attention_kernel = "decode_stream_kernel" if balanced else "decode_partition_kernel"
     decode_ms_mean = sum(decode_ms) / len(decode_ms)
@@ -381,7 +413,8 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {
-            "workload": WORKLOAD_NAMES[cfg] + (f", sliding window {args.window}" if args.window else ""),
+            "workload": WORKLOAD_NAMES[cfg] + (f", sliding window {args.window}" if args.window else "")
+                        + (", FP8 (E4M3) pools" if args.fp8 else ""),
             "seed": seed,
             "num_seqs": w.num_seqs,
             "sum_context_tokens": int(w.context_lens.sum()),
@@ -391,13 +424,14 @@ def main():
             "pool_copies_rotated": reps,
             "partition_tokens": args.partition or "auto",
             "step_calls": ("pa_append_decode" if fused else
-                           ("pa_write_kv + " if writes else "") +
-                           ("pa_decode_sliding" if args.window else "pa_decode")),
+                           ("pa_write_kv_fp8 + pa_decode_fp8" if args.fp8 else
+                            ("pa_write_kv + " if writes else "") +
+                            ("pa_decode_sliding" if args.window else "pa_decode"))),
         },
         "roofline": {
             "bound": "hbm",
             "kernel": (attention_kernel + " (attention kernel of " +
-                       ("pa_append_decode" if fused else
+                       ("pa_append_decode" if fused else "pa_decode_fp8" if args.fp8 else
                         "pa_decode_sliding" if args.window else "pa_decode") + ")"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -422,7 +456,8 @@ def main():
             "kernel_us_mean": round(two_kernel_us, 2),
         }
     if not args.no_cpu_baseline:
-        v, sample, cores = cpu_baseline(w, args.cpu_seconds, args.window)
+        v, sample, cores = cpu_baseline(w, args.cpu_seconds, args.window,
+                                        (ks, vs) if args.fp8 else None)
         result["cpu_baseline"] = {"value": round(v, 6), "unit": "TB/s", "cores": cores,
                                   "kind": "oracle", "sample": sample}
     print(json.dumps(result), flush=True)
