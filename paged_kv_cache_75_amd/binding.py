@@ -16,8 +16,7 @@ import re
 # PA_LIBRARY selects another build of the same library (A/B measurements)
 LIB_PATH = os.environ.get("PA_LIBRARY") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "_lib", "libpa.so")
-HEADER_PATH = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
-                           "include", "paged_attention.h")
+INCLUDE_DIR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include")
 
 PA_OK = 0
 PA_ERR_INVALID_ARGUMENT = 1
@@ -43,11 +42,15 @@ class pa_pool_desc(ctypes.Structure):
 _lib = None
 
 
-def declared_functions(header: str = HEADER_PATH) -> list[str]:
-    """Names of the functions include/paged_attention.h declares."""
-    text = open(header).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+def declared_functions(include_dir: str = INCLUDE_DIR) -> list[str]:
+    """Names of the functions the headers under include/ declare."""
+    names = set()
+    for h in sorted(os.listdir(include_dir)):
+        if h.endswith(".h"):
+            text = open(os.path.join(include_dir, h)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def lib():
