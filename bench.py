@@ -57,6 +57,10 @@ def parse():
     ap.add_argument("--prefill", type=int, default=0,
                     help="chunked prefill instead of decode: every sequence of the first 16 of "
                          "the Llama-3-8B batch gets a chunk of this many new tokens (pa_prefill)")
+    ap.add_argument("--cow", type=int, default=0,
+                    help="copy-on-write instead of decode: one pa_copy_blocks launch copying "
+                         "this many shared blocks in all 64 pools of Llama-3-8B (32 layers, K "
+                         "and V), plus the host block manager's cost for the same batch")
     ap.add_argument("--fp8", action="store_true",
                     help="FP8 (E4M3) pools with per-pool scales: pa_write_kv_fp8 + pa_decode_fp8")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
@@ -247,6 +251,139 @@ def prefill_main(args):
     print(json.dumps(result), flush=True)
 
 
+def cow_main(args):
+    """Copy-on-write: N sequences each write into a block they share, so N
+    (source, destination) block pairs are copied in every pool of the model:
+    32 layers x (K, V) = 64 pools of [2048][8][16][128] bf16 (32 KiB per
+    block).  Step = one pa_copy_blocks launch; unit: bytes moved (each block
+    read once and written once).  Steps rotate over several pair sets so
+    the reads stay cold in the caches.  The native block manager's host time
+    for the batch that produces the pairs is reported beside it."""
+    import numpy as np
+    import torch
+
+    import oracle.block_manager_ref as bm_ref
+    from paged_kv_cache_75_amd import (BlockManager, pa_copy_blocks, pa_profile_start,
+                                       pa_profile_stop)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    N = args.cow
+    layers, nb, hkv, bs, hd = 32, 2048, 8, 16, 128
+    if 2 * N > nb:
+        sys.exit(f"--cow {N}: at most {nb // 2} pairs")
+    block_bytes = hkv * bs * hd * 2
+    pools = [torch.empty((nb, hkv, bs, hd), dtype=torch.bfloat16, device=dev)
+             for _ in range(2 * layers)]
+    g = torch.Generator(device=dev)
+    g.manual_seed(args.seed or 7)
+    for p in pools:
+        p.normal_(generator=g)
+    moved = 2 * N * len(pools) * block_bytes                  # read + write per launch
+    sets = max(1, min(16, -(-(2 << 30) // moved)))
+    rng = np.random.default_rng(args.seed or 7)
+    maps = []
+    for _ in range(sets):
+        perm = rng.permutation(nb)
+        maps.append(torch.from_numpy(np.stack([perm[N:2 * N], perm[:N]], 1).astype(np.int32))
+                    .to(dev))
+
+    def step(k):
+        pa_copy_blocks(pools, maps[k % sets])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    pa_profile_start()
+    for k in range(args.steps):
+        step(k)
+    torch.cuda.synchronize()
+    launches, kernel_us = pa_profile_stop()
+    assert launches == args.steps, (launches, args.steps)
+    # the last launch copied maps[(steps - 1) % sets]: destinations equal sources
+    last = maps[(args.steps - 1) % sets].long()
+    for p in (pools[0], pools[-1]):
+        assert torch.equal(p[last[:, 1]], p[last[:, 0]]), "copied blocks differ from sources"
+
+    # the host side of the same batch: N sequence pairs (a prompt of ~400
+    # tokens and a fork of it); one member of each pair appends a token into
+    # the shared partial block (N copy-on-write pairs), then 15 plain batches
+    prompt_rng = np.random.default_rng(5)
+    prompts = [prompt_rng.integers(0, 32000, 400 + i % 7 + 1) for i in range(N)]
+    seqs = np.arange(0, 2 * N, 2)
+    cow_s, plain_s, plain_n = 0.0, 0.0, 0
+    for _ in range(10):
+        m = BlockManager(2 * N * 32 + 64, bs)
+        for i in range(N):
+            m.allocate(2 * i, prompts[i])
+            m.fork(2 * i, 2 * i + 1)
+        t = time.perf_counter()
+        _, pairs = m.append(seqs, np.full(N, 11))
+        cow_s += time.perf_counter() - t
+        assert len(pairs) == N
+        for _ in range(15):
+            t = time.perf_counter()
+            m.append(seqs, np.full(N, 12))
+            plain_s += time.perf_counter() - t
+            plain_n += 1
+    sys_prompt = prompt_rng.integers(0, 32000, 1800)
+    m2 = BlockManager(8192, bs)
+    m2.allocate(0, np.concatenate([sys_prompt, [1]]))
+    t = time.perf_counter()
+    for i in range(1, 101):
+        assert m2.allocate(i, np.concatenate([sys_prompt, [i + 1]])) == 112 * bs
+    alloc_us = (time.perf_counter() - t) * 1e6 / 100
+
+    achieved = moved / (kernel_us * 1e-6) / 1e9
+    result = {
+        "metric": "copy-on-write block copy: bytes moved/s (TB/s, read + write), us/step",
+        "value": round(moved / (ms * 1e-3) / 1e12, 4),
+        "unit": "TB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"llama3-8b-cow-bf16: {N} block pairs x 64 pools (32 layers x K/V) "
+                               f"of [2048][8][16][128], 32 KiB per block",
+                   "pairs": N, "pools": len(pools), "block_bytes": block_bytes,
+                   "bytes_moved_per_step": moved, "pair_sets_rotated": sets,
+                   "step_calls": "pa_copy_blocks"},
+        "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel (pa_copy_blocks)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel_us_mean": round(kernel_us, 2), "kernel_launches_timed": launches},
+        "host_block_manager": {
+            "append_batch_cow_us": round(cow_s * 1e6 / 10, 2),
+            "append_batch_us": round(plain_s * 1e6 / plain_n, 2),
+            "append_batch": f"{N} sequences, one token each; the copy-on-write batch has every "
+                            f"sequence write into a block it shares with a fork ({N} pairs)",
+            "allocate_prefix_hit_us": round(alloc_us, 2),
+            "allocate": "1801-token prompt, 112 of 113 blocks hit (1800-token shared prefix)",
+        },
+    }
+    if not args.no_cpu_baseline:
+        # the oracle's block copy on host pools of the same block shape (64
+        # pools of 4 * N blocks), N pairs per call, one thread
+        host = [np.zeros((2 * N + 2, hkv, bs, hd), np.uint16) for _ in range(2 * layers)]
+        pairs = [(i, N + i) for i in range(N)]
+        done, secs, calls = 0, 0.0, 0
+        while secs < min(args.cpu_seconds, 10.0):
+            t = time.perf_counter()
+            bm_ref.copy_blocks(host, pairs, inplace=True)
+            secs += time.perf_counter() - t
+            done += moved
+            calls += 1
+        result["cpu_baseline"] = {"value": round(done / secs / 1e12, 6), "unit": "TB/s",
+                                  "cores": 1, "kind": "oracle",
+                                  "sample": f"{calls} calls of the oracle's copy_blocks, {N} pairs "
+                                            f"x 64 host pools, {secs:.1f} s"}
+    print(json.dumps(result), flush=True)
+
+
 def main():
     args = parse()
     if args.copy_calibration:
@@ -270,6 +407,9 @@ def main():
         sys.exit("bench.py needs a GPU")
     if args.prefill:
         prefill_main(args)
+        return
+    if args.cow:
+        cow_main(args)
         return
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)

@@ -53,7 +53,9 @@ typedef enum pa_status {
   PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size */
   PA_ERR_UNSUPPORTED = 2,        /* a valid shape this build does not handle   */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
-  PA_ERR_HIP = 4                 /* a HIP runtime call or a launch failed      */
+  PA_ERR_HIP = 4,                /* a HIP runtime call or a launch failed      */
+  PA_ERR_OUT_OF_BLOCKS = 5,      /* block manager: not enough free blocks      */
+  PA_ERR_HOST_MEMORY = 6         /* block manager: a host allocation failed    */
 } pa_status;
 
 typedef enum pa_dtype {
@@ -264,12 +266,43 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
                      void* stream);
 
 /*
+ * pa_copy_blocks -- copy whole physical blocks, the copy behind copy-on-write
+ * ("vLLM Framework and Inference Engine Design", section "What operations can
+ * cause memory fragmentation, and how does vLLM avoid it?": a block shared
+ * through reference counts is copied only when a sequence has to write into
+ * it; bibekananda.in, "vLLM", section "The part that is easy to miss": the
+ * writer gets a fresh block and the shared one stays untouched).  One call
+ * copies the same block pairs in every given pool, e.g. the K and V pools of
+ * every layer of a model, in one launch.
+ *
+ *   pools         HOST array of num_pools DEVICE pointers (16-byte aligned);
+ *                 each pool is num_blocks blocks of block_bytes bytes (a
+ *                 pa_pool_desc pool has block_bytes = num_kv_heads *
+ *                 block_size * head_dim * element bytes, 1 byte for FP8).
+ *   block_bytes   a positive multiple of 16, at most 2^30.
+ *   block_mapping DEVICE int32 [num_pairs][2]: (source, destination).  For
+ *                 every pool, destination block = source block, raw bytes.
+ *                 A pair with an entry outside [0, num_blocks) is skipped.
+ *                 Contract: destinations are distinct and none is a source
+ *                 (a copy-on-write destination is always a fresh block);
+ *                 otherwise the affected blocks are unspecified.
+ *   num_pools     >= 1; num_pairs >= 0 (0: nothing is enqueued).
+ *
+ * The pool pointers are passed by value to the kernel (64 pools per launch;
+ * more pools take more launches), so the call allocates nothing.
+ */
+pa_status pa_copy_blocks(void* const* pools, int32_t num_pools, int32_t num_blocks,
+                         int64_t block_bytes, const int32_t* block_mapping, int32_t num_pairs,
+                         void* stream);
+
+/*
  * pa_profile_start / pa_profile_stop -- kernel timing for measurements; not
  * needed to compute anything.  Between the two calls, every pa_decode,
  * pa_append_decode, pa_decode_sliding and pa_prefill call launches its
  * attention kernel (the balanced-split stream kernel, the fixed-partition
- * kernel, or the prefill kernel) with a HIP start and stop event attached to
- * that dispatch; the piece merge is not included.  pa_profile_stop
+ * kernel, or the prefill kernel), and every pa_copy_blocks launch, with a
+ * HIP start and stop event attached to that dispatch; the piece merge is not
+ * included.  pa_profile_stop
  * turns timing off, waits for the recorded events, and returns how many
  * launches were timed and their mean duration in microseconds (0 launches:
  * mean 0).  The switch is process-wide; while it is on each call creates two

@@ -23,6 +23,8 @@ PA_ERR_INVALID_ARGUMENT = 1
 PA_ERR_UNSUPPORTED = 2
 PA_ERR_WORKSPACE_TOO_SMALL = 3
 PA_ERR_HIP = 4
+PA_ERR_OUT_OF_BLOCKS = 5
+PA_ERR_HOST_MEMORY = 6
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 
@@ -83,6 +85,18 @@ def lib():
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
         "pa_status_string": ([c_int], ctypes.c_char_p),
+        "pa_copy_blocks": ([ctypes.POINTER(vp), i32, i32, ctypes.c_int64, vp, i32, vp], c_int),
+        "pa_bm_create": ([i32, i32, i32, ctypes.POINTER(vp)], c_int),
+        "pa_bm_destroy": ([vp], None),
+        "pa_bm_allocate": ([vp, ctypes.c_int64, vp, i32, vp, i32, vp], c_int),
+        "pa_bm_append": ([vp, vp, vp, i32, vp, vp, vp], c_int),
+        "pa_bm_fork": ([vp, ctypes.c_int64, ctypes.c_int64], c_int),
+        "pa_bm_free": ([vp, ctypes.c_int64], c_int),
+        "pa_bm_tables": ([vp, vp, i32, i32, vp, vp], c_int),
+        "pa_bm_num_free": ([vp], i32),
+        "pa_bm_block_info": ([vp, i32, vp, vp, vp, vp], c_int),
+        "pa_bm_free_queue": ([vp, vp, i32, vp], c_int),
+        "pa_sha256": ([vp, sz, vp], c_int),
     }
     # a symbol the library lacks stays undeclared: calling it raises
     # AttributeError (tests/test_abi.py checks that every one is exported)
@@ -383,3 +397,158 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
     if st != PA_OK:
         raise PaError(st, where)
     return out
+
+
+# ---------------------------------------------------------------------------
+# block copy (copy-on-write) and the host block manager
+# ---------------------------------------------------------------------------
+def pa_copy_blocks(pools, block_mapping, stream=None) -> None:
+    """For every (source, destination) row of ``block_mapping`` (int32 [n][2]
+    on the pools' device), copy block source to block destination in every
+    pool of ``pools`` (tensors of one shape and dtype; axis 0 is the block)."""
+    torch = _torch()
+    pools = list(pools)
+    if not pools:
+        raise ValueError("no pools")
+    ref = pools[0]
+    if ref.dim() < 1:
+        raise ValueError("pools need a block axis")
+    for i, t in enumerate(pools):
+        _check(t, f"pools[{i}]", dtype=ref.dtype, device=ref.device)
+        if t.shape != ref.shape:
+            raise ValueError("pools differ in shape")
+    _check(block_mapping, "block_mapping", dtype=torch.int32, device=ref.device)
+    if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
+        raise ValueError("block_mapping must be [num_pairs][2]")
+    num_blocks = int(ref.shape[0])
+    block_bytes = (ref.numel() // num_blocks) * ref.element_size() if num_blocks else 16
+    ptrs = (ctypes.c_void_p * len(pools))(*[t.data_ptr() for t in pools])
+    st = lib().pa_copy_blocks(ptrs, len(pools), num_blocks, block_bytes,
+                              block_mapping.data_ptr(), int(block_mapping.shape[0]),
+                              _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_copy_blocks")
+
+
+def pa_sha256(data: bytes) -> bytes:
+    out = (ctypes.c_uint8 * 32)()
+    buf = ctypes.create_string_buffer(bytes(data), len(data)) if data else None
+    st = lib().pa_sha256(buf, len(data), out)
+    if st != PA_OK:
+        raise PaError(st, "pa_sha256")
+    return bytes(out)
+
+
+class OutOfBlocks(PaError):
+    """Not enough free blocks (the manager is unchanged)."""
+
+
+class BlockManager:
+    """The library's host block manager (free queue, reference counts,
+    chained prefix hashes, copy-on-write).  Host-side NumPy in and out."""
+
+    def __init__(self, num_blocks: int, block_size: int, prefix_caching: bool = True):
+        h = ctypes.c_void_p()
+        st = lib().pa_bm_create(int(num_blocks), int(block_size), int(bool(prefix_caching)),
+                                ctypes.byref(h))
+        if st != PA_OK:
+            raise PaError(st, "pa_bm_create")
+        self._h = h
+        self.num_blocks = int(num_blocks)
+        self.block_size = int(block_size)
+
+    def close(self) -> None:
+        if self._h:
+            lib().pa_bm_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def _raise(self, st, where):
+        if st == PA_ERR_OUT_OF_BLOCKS:
+            raise OutOfBlocks(st, where)
+        if st != PA_OK:
+            raise PaError(st, where)
+
+    def allocate(self, seq: int, prompt, salt: bytes = b"") -> int:
+        """Admit ``seq``; returns the number of prompt tokens already cached."""
+        import numpy as np
+        toks = np.ascontiguousarray(np.asarray(prompt, dtype=np.int32).reshape(-1))
+        cached = ctypes.c_int32(0)
+        salt = bytes(salt)
+        sbuf = ctypes.create_string_buffer(salt, len(salt)) if salt else None
+        st = lib().pa_bm_allocate(self._h, int(seq), toks.ctypes.data if toks.size else None,
+                                  int(toks.size), sbuf, len(salt), ctypes.byref(cached))
+        self._raise(st, "pa_bm_allocate")
+        return int(cached.value)
+
+    def append(self, seqs, tokens):
+        """Append tokens[i] to seqs[i] (in order); returns (slots int32 [n],
+        copy-on-write pairs int32 [k][2])."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
+        toks = np.ascontiguousarray(np.asarray(tokens, dtype=np.int32).reshape(-1))
+        if ids.size != toks.size:
+            raise ValueError("seqs and tokens differ in length")
+        n = int(ids.size)
+        slots = np.zeros(max(n, 1), np.int32)
+        pairs = np.zeros((max(n, 1), 2), np.int32)
+        k = ctypes.c_int32(0)
+        st = lib().pa_bm_append(self._h, ids.ctypes.data, toks.ctypes.data, n, slots.ctypes.data,
+                                pairs.ctypes.data, ctypes.byref(k))
+        self._raise(st, "pa_bm_append")
+        return slots[:n].copy(), pairs[:k.value].copy()
+
+    def append_one(self, seq: int, token: int):
+        """One token; returns (slot, (source, destination) or None)."""
+        slots, pairs = self.append([seq], [token])
+        return int(slots[0]), (tuple(int(x) for x in pairs[0]) if len(pairs) else None)
+
+    def fork(self, parent: int, child: int) -> None:
+        self._raise(lib().pa_bm_fork(self._h, int(parent), int(child)), "pa_bm_fork")
+
+    def free_seq(self, seq: int) -> None:
+        self._raise(lib().pa_bm_free(self._h, int(seq)), "pa_bm_free")
+
+    def tables(self, seqs, max_blocks: int):
+        """(block tables int32 [n][max_blocks] padded with -1, context lengths)."""
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(seqs, dtype=np.int64).reshape(-1))
+        tab = np.zeros((ids.size, max_blocks), np.int32)
+        lens = np.zeros(ids.size, np.int32)
+        st = lib().pa_bm_tables(self._h, ids.ctypes.data, int(ids.size), int(max_blocks),
+                                tab.ctypes.data, lens.ctypes.data)
+        self._raise(st, "pa_bm_tables")
+        return tab, lens
+
+    def block_table(self, seq: int) -> list[int]:
+        tab, _ = self.tables([seq], self.num_blocks)
+        row = tab[0]
+        return [int(b) for b in row[row >= 0]]
+
+    def num_tokens(self, seq: int) -> int:
+        return int(self.tables([seq], self.num_blocks)[1][0])
+
+    def num_free(self) -> int:
+        return int(lib().pa_bm_num_free(self._h))
+
+    def block_info(self, block: int):
+        """(reference count, digest bytes or None, registered)."""
+        ref, has, reg = ctypes.c_int32(0), ctypes.c_int32(0), ctypes.c_int32(0)
+        d = (ctypes.c_uint8 * 32)()
+        st = lib().pa_bm_block_info(self._h, int(block), ctypes.byref(ref), ctypes.byref(has), d,
+                                    ctypes.byref(reg))
+        self._raise(st, "pa_bm_block_info")
+        return int(ref.value), (bytes(d) if has.value else None), bool(reg.value)
+
+    def free_queue(self) -> list[int]:
+        import numpy as np
+        out = np.zeros(max(self.num_blocks, 1), np.int32)
+        n = ctypes.c_int32(0)
+        st = lib().pa_bm_free_queue(self._h, out.ctypes.data, self.num_blocks, ctypes.byref(n))
+        self._raise(st, "pa_bm_free_queue")
+        return [int(b) for b in out[:n.value]]

@@ -1,5 +1,7 @@
 // C entry points of libpa: validate on the host, plan, launch on the
 // caller's stream.  Nothing here allocates or synchronizes.
+#include <algorithm>
+#include <climits>
 #include <cmath>
 
 #include <hip/hip_runtime_api.h>
@@ -30,6 +32,33 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
   a.log2_block = lb;
   return pa::launch_write_kv(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
                                                                                 : PA_ERR_HIP;
+}
+
+pa_status pa_copy_blocks(void* const* pools, int32_t num_pools, int32_t num_blocks,
+                         int64_t block_bytes, const int32_t* block_mapping, int32_t num_pairs,
+                         void* stream) {
+  if (!pools || num_pools < 1 || num_blocks < 0 || num_pairs < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (block_bytes <= 0 || block_bytes % 16 != 0 || block_bytes > (int64_t(1) << 30))
+    return PA_ERR_INVALID_ARGUMENT;
+  if (num_pairs > 0 && !block_mapping) return PA_ERR_INVALID_ARGUMENT;
+  for (int32_t i = 0; i < num_pools; ++i)
+    if (!pools[i] || reinterpret_cast<uintptr_t>(pools[i]) % 16 != 0)
+      return PA_ERR_INVALID_ARGUMENT;
+  const int64_t chunks = pa::copy_chunks_per_block(block_bytes);
+  if (int64_t(num_pairs) * chunks > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  if (num_pairs == 0 || num_blocks == 0) return PA_OK;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t done = 0; done < num_pools; done += pa::kCopyMaxPools) {
+    pa::CopyArgs a{};
+    const int32_t n = std::min<int32_t>(pa::kCopyMaxPools, num_pools - done);
+    for (int32_t i = 0; i < n; ++i) a.pools[i] = static_cast<char*>(pools[done + i]);
+    a.mapping = block_mapping;
+    a.block_bytes = block_bytes;
+    a.num_blocks = num_blocks;
+    a.chunks = static_cast<int32_t>(chunks);
+    if (pa::launch_copy_blocks(a, num_pairs, n, s) != hipSuccess) return PA_ERR_HIP;
+  }
+  return PA_OK;
 }
 
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
@@ -244,6 +273,8 @@ const char* pa_status_string(pa_status status) {
     case PA_ERR_UNSUPPORTED: return "PA_ERR_UNSUPPORTED";
     case PA_ERR_WORKSPACE_TOO_SMALL: return "PA_ERR_WORKSPACE_TOO_SMALL";
     case PA_ERR_HIP: return "PA_ERR_HIP";
+    case PA_ERR_OUT_OF_BLOCKS: return "PA_ERR_OUT_OF_BLOCKS";
+    case PA_ERR_HOST_MEMORY: return "PA_ERR_HOST_MEMORY";
     default: return "PA_UNKNOWN_STATUS";
   }
 }

@@ -68,6 +68,24 @@ struct DecodeArgs {
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);
 
+// Block copy: pools travel by value in the kernel arguments, up to
+// kCopyMaxPools per launch.  A workgroup moves one chunk of kCopyChunkBytes of
+// one block of one pool.
+constexpr int32_t kCopyMaxPools = 64;
+constexpr int64_t kCopyChunkBytes = 16384;
+inline int64_t copy_chunks_per_block(int64_t block_bytes) {
+  return (block_bytes + kCopyChunkBytes - 1) / kCopyChunkBytes;
+}
+struct CopyArgs {
+  char* pools[kCopyMaxPools];
+  const int32_t* mapping;      // [num_pairs][2] (source, destination)
+  int64_t block_bytes;         // multiple of 16
+  int32_t num_blocks;
+  int32_t chunks;              // copy_chunks_per_block(block_bytes)
+};
+hipError_t launch_copy_blocks(const CopyArgs& a, int32_t num_pairs, int32_t num_pools,
+                              hipStream_t stream);
+
 // Slot write into FP8 (E4M3) pools; a.row_bytes = head_dim (one byte per
 // code); dtype = element type of k and v.
 hipError_t launch_write_kv_fp8(const WriteArgs& a, int32_t dtype, float k_scale, float v_scale,

@@ -206,6 +206,44 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// block copy (copy-on-write): workgroup (x, y) moves chunk x % chunks of pair
+// x / chunks in pool y.  In a whole chunk each thread issues its four 16-byte
+// loads before its stores, so a workgroup keeps 16 KiB in flight; the last,
+// partial chunk of a block copies one vector at a time.
+// ---------------------------------------------------------------------------
+constexpr int kCopyThreads = 256;
+constexpr int kCopyVecs = int(kCopyChunkBytes / (16 * kCopyThreads));
+
+__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
+  const int pair = blockIdx.x / a.chunks;
+  const int chunk = blockIdx.x - pair * a.chunks;
+  const int32_t src = a.mapping[2 * pair];
+  const int32_t dst = a.mapping[2 * pair + 1];
+  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
+  char* pool = a.pools[blockIdx.y];
+  const uint4* from = reinterpret_cast<const uint4*>(pool + int64_t(src) * a.block_bytes);
+  uint4* to = reinterpret_cast<uint4*>(pool + int64_t(dst) * a.block_bytes);
+  const int64_t vecs = a.block_bytes / 16;
+  const int64_t first = int64_t(chunk) * (kCopyThreads * kCopyVecs);
+  if (first + kCopyThreads * kCopyVecs <= vecs) {
+    // a whole chunk (the same branch for the whole workgroup)
+    // four named registers: an array here is turned into LDS by the compiler
+    static_assert(kCopyVecs == 4, "one register per vector below");
+    const int64_t i = first + threadIdx.x;
+    const uint4 v0 = from[i];
+    const uint4 v1 = from[i + kCopyThreads];
+    const uint4 v2 = from[i + 2 * kCopyThreads];
+    const uint4 v3 = from[i + 3 * kCopyThreads];
+    to[i] = v0;
+    to[i + kCopyThreads] = v1;
+    to[i + 2 * kCopyThreads] = v2;
+    to[i + 3 * kCopyThreads] = v3;
+  } else {
+    for (int64_t i = first + threadIdx.x; i < vecs; i += kCopyThreads) to[i] = from[i];
+  }
+}
+
 // FP8 pools: E4M3 code of a float32 value y = x / scale, rounded to nearest
 // with ties to an even mantissa; 448 and above (infinities too) saturate to
 // 448, NaN stays NaN.  Written from the OCP 8-bit floating point definition:
@@ -1861,6 +1899,14 @@ hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   hipLaunchKernelGGL(write_kv_kernel, dim3(a.num_tokens), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_blocks(const CopyArgs& a, int32_t num_pairs, int32_t num_pools,
+                              hipStream_t stream) {
+  if (num_pairs == 0 || num_pools == 0) return hipSuccess;
+  launch_attention(copy_blocks_kernel, dim3(num_pairs * a.chunks, num_pools), dim3(kCopyThreads),
+                   stream, a);
   return hipGetLastError();
 }
 

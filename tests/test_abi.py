@@ -14,8 +14,9 @@ pytestmark = pytest.mark.skipif(not os.path.exists(B.LIB_PATH), reason="libpa.so
 def test_exports_every_declared_function():
     names = B.declared_functions()
     assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding", "pa_prefill",
-            "pa_write_kv_fp8", "pa_decode_fp8",
-            "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
+            "pa_write_kv_fp8", "pa_decode_fp8", "pa_copy_blocks", "pa_bm_create",
+            "pa_bm_allocate", "pa_bm_append", "pa_bm_fork", "pa_bm_free", "pa_bm_tables",
+            "pa_sha256", "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
             "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
@@ -24,7 +25,8 @@ def test_exports_every_declared_function():
 
 def test_status_strings():
     for code, name in ((0, "PA_OK"), (1, "PA_ERR_INVALID_ARGUMENT"), (2, "PA_ERR_UNSUPPORTED"),
-                       (3, "PA_ERR_WORKSPACE_TOO_SMALL"), (4, "PA_ERR_HIP")):
+                       (3, "PA_ERR_WORKSPACE_TOO_SMALL"), (4, "PA_ERR_HIP"),
+                       (5, "PA_ERR_OUT_OF_BLOCKS"), (6, "PA_ERR_HOST_MEMORY")):
         assert B.pa_status_string(code) == name
     assert B.pa_status_string(99) == "PA_UNKNOWN_STATUS"
 
@@ -211,3 +213,32 @@ def test_write_kv_fp8_validation(ks, vs, want):
     d = desc()
     assert B.lib().pa_write_kv_fp8(FAKE, FAKE, FAKE, 4, FAKE, FAKE, ctypes.byref(d), ks, vs,
                                    None) == want
+
+
+def _copy(pools=(FAKE, FAKE), num_pools=None, nb=64, bb=32768, mapping=FAKE, n=4):
+    if pools is None:
+        arr, count = None, 2
+    else:
+        arr, count = (ctypes.c_void_p * len(pools))(*pools), len(pools)
+    return B.lib().pa_copy_blocks(arr, count if num_pools is None else num_pools, nb, bb,
+                                  mapping, n, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(pools=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(num_pools=0), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(pools=(FAKE, None)), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(pools=(FAKE, FAKE + 8)), B.PA_ERR_INVALID_ARGUMENT),     # not 16-byte aligned
+    (dict(nb=-1), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(bb=0), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(bb=40), B.PA_ERR_INVALID_ARGUMENT),                     # not a multiple of 16
+    (dict(bb=(1 << 30) + 16), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(mapping=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(n=-1), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(n=2**31 - 1, bb=1 << 20), B.PA_ERR_UNSUPPORTED),        # grid limit
+    (dict(n=0), B.PA_OK),                                         # nothing enqueued
+    (dict(n=0, mapping=None), B.PA_OK),
+    (dict(nb=0), B.PA_OK),
+])
+def test_copy_blocks_validation(kw, want):
+    assert _copy(**kw) == want
