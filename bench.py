@@ -121,23 +121,30 @@ def cpu_baseline(w, budget_s: float, window: int = 0, fp8_scales=None):
 
 
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama3-8b-bf16.json")
+COPY_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "copy_blocks_llama3-8b-cow256-bf16.json")
 
 
-def profiled_traffic(cfg):
-    """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 counter summary, or None when it does not describe the kernel
-    as built now (the summary records the kernel source's sha256)."""
+def summary_traffic(path, source):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    summary, or None when the summary does not describe the kernel as built
+    now (it records the sha256 of the kernel's source file)."""
     import hashlib
-    if cfg != 3 or not os.path.exists(PROFILE_SUMMARY):
+    if not os.path.exists(path):
         return None, None
-    with open(PROFILE_SUMMARY) as f:
+    with open(path) as f:
         prof = json.load(f)
-    src = os.path.join(ROOT, "paged_kv_cache_75_amd", "csrc", "pa_kernels.hip")
-    with open(src, "rb") as f:
+    with open(os.path.join(ROOT, "paged_kv_cache_75_amd", "csrc", source), "rb") as f:
         sha = hashlib.sha256(f.read()).hexdigest()
     if sha != prof.get("kernel_source_sha256"):
         return None, None
     return prof["traffic_bytes_per_launch"], prof
+
+
+def profiled_traffic(cfg):
+    """Traffic of the decode step's attention kernel (configuration 3 only)."""
+    if cfg != 3:
+        return None, None
+    return summary_traffic(PROFILE_SUMMARY, "pa_kernels.hip")
 
 
 def kv_bytes_per_step(w, window: int = 0) -> int:
@@ -263,7 +270,7 @@ def cow_main(args):
     import torch
 
     import oracle.block_manager_ref as bm_ref
-    from paged_kv_cache_75_amd import (BlockManager, pa_copy_blocks, pa_profile_start,
+    from paged_kv_cache_75_amd import (BlockManager, PoolSet, pa_copy_blocks, pa_profile_start,
                                        pa_profile_stop)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
@@ -287,8 +294,10 @@ def cow_main(args):
         maps.append(torch.from_numpy(np.stack([perm[N:2 * N], perm[:N]], 1).astype(np.int32))
                     .to(dev))
 
+    pool_set = PoolSet(pools)
+
     def step(k):
-        pa_copy_blocks(pools, maps[k % sets])
+        pa_copy_blocks(pool_set, maps[k % sets])
 
     for k in range(args.warmup):
         step(k)
@@ -304,6 +313,21 @@ def cow_main(args):
     torch.cuda.synchronize()
     launches, kernel_us = pa_profile_stop()
     assert launches == args.steps, (launches, args.steps)
+    # a torch device copy of the same byte count, timed the same way, as the
+    # practical ceiling of a copy on this GPU
+    src = torch.empty(moved // 2, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(3)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    torch_copy_us = e0.elapsed_time(e1) * 1e3 / 10
+    del src, dst
     # the last launch copied maps[(steps - 1) % sets]: destinations equal sources
     last = maps[(args.steps - 1) % sets].long()
     for p in (pools[0], pools[-1]):
@@ -339,6 +363,7 @@ def cow_main(args):
     alloc_us = (time.perf_counter() - t) * 1e6 / 100
 
     achieved = moved / (kernel_us * 1e-6) / 1e9
+    traffic_bytes, _ = summary_traffic(COPY_PROFILE_SUMMARY, "pa_copy.hip") if N == 256 else (None, None)
     result = {
         "metric": "copy-on-write block copy: bytes moved/s (TB/s, read + write), us/step",
         "value": round(moved / (ms * 1e-3) / 1e12, 4),
@@ -354,8 +379,15 @@ def cow_main(args):
                    "step_calls": "pa_copy_blocks"},
         "roofline": {"bound": "hbm", "kernel": "copy_blocks_kernel (pa_copy_blocks)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel_us_mean": round(kernel_us, 2), "kernel_launches_timed": launches},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if traffic_bytes is None else round(traffic_bytes),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "traffic_source": (os.path.relpath(COPY_PROFILE_SUMMARY, ROOT)
+                                        if traffic_bytes is not None else None),
+                     "kernel_us_mean": round(kernel_us, 2), "kernel_launches_timed": launches,
+                     "torch_copy_same_bytes_us": round(torch_copy_us, 2),
+                     "torch_copy_GBps": round(moved / (torch_copy_us * 1e-6) / 1e9, 1)},
         "host_block_manager": {
             "append_batch_cow_us": round(cow_s * 1e6 / 10, 2),
             "append_batch_us": round(plain_s * 1e6 / plain_n, 2),

@@ -402,28 +402,43 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
 # ---------------------------------------------------------------------------
 # block copy (copy-on-write) and the host block manager
 # ---------------------------------------------------------------------------
+class PoolSet:
+    """Pools for pa_copy_blocks, checked once: tensors of one shape and dtype
+    on one device, axis 0 the block.  Keeps the C array of their pointers, so
+    a step that copies blocks in every layer's pools pays no per-pool work."""
+
+    def __init__(self, pools):
+        pools = list(pools)
+        if not pools:
+            raise ValueError("no pools")
+        ref = pools[0]
+        if ref.dim() < 1:
+            raise ValueError("pools need a block axis")
+        for i, t in enumerate(pools):
+            _check(t, f"pools[{i}]", dtype=ref.dtype, device=ref.device)
+            if t.shape != ref.shape:
+                raise ValueError("pools differ in shape")
+        self.pools = pools                   # keeps the tensors alive
+        self.device = ref.device
+        self.num_blocks = int(ref.shape[0])
+        self.block_bytes = ((ref.numel() // self.num_blocks) * ref.element_size()
+                            if self.num_blocks else 16)
+        self.ptrs = (ctypes.c_void_p * len(pools))(*[t.data_ptr() for t in pools])
+
+    def __len__(self):
+        return len(self.pools)
+
+
 def pa_copy_blocks(pools, block_mapping, stream=None) -> None:
     """For every (source, destination) row of ``block_mapping`` (int32 [n][2]
     on the pools' device), copy block source to block destination in every
-    pool of ``pools`` (tensors of one shape and dtype; axis 0 is the block)."""
+    pool (a PoolSet, or a list of tensors of one shape and dtype)."""
     torch = _torch()
-    pools = list(pools)
-    if not pools:
-        raise ValueError("no pools")
-    ref = pools[0]
-    if ref.dim() < 1:
-        raise ValueError("pools need a block axis")
-    for i, t in enumerate(pools):
-        _check(t, f"pools[{i}]", dtype=ref.dtype, device=ref.device)
-        if t.shape != ref.shape:
-            raise ValueError("pools differ in shape")
-    _check(block_mapping, "block_mapping", dtype=torch.int32, device=ref.device)
+    ps = pools if isinstance(pools, PoolSet) else PoolSet(pools)
+    _check(block_mapping, "block_mapping", dtype=torch.int32, device=ps.device)
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [num_pairs][2]")
-    num_blocks = int(ref.shape[0])
-    block_bytes = (ref.numel() // num_blocks) * ref.element_size() if num_blocks else 16
-    ptrs = (ctypes.c_void_p * len(pools))(*[t.data_ptr() for t in pools])
-    st = lib().pa_copy_blocks(ptrs, len(pools), num_blocks, block_bytes,
+    st = lib().pa_copy_blocks(ps.ptrs, len(ps), ps.num_blocks, ps.block_bytes,
                               block_mapping.data_ptr(), int(block_mapping.shape[0]),
                               _stream(stream))
     if st != PA_OK:

@@ -19,6 +19,7 @@
 #include <vector>
 
 #include "pa_kernels.h"
+#include "pa_launch.h"
 
 namespace pa {
 
@@ -203,44 +204,6 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
     char* dst = static_cast<char*>(is_v ? a.v_pool : a.k_pool) +
                 ((blk * a.num_kv_heads + h) << a.log2_block | off) * a.row_bytes;
     reinterpret_cast<uint4*>(dst)[ch] = reinterpret_cast<const uint4*>(src)[ch];
-  }
-}
-
-// ---------------------------------------------------------------------------
-// block copy (copy-on-write): workgroup (x, y) moves chunk x % chunks of pair
-// x / chunks in pool y.  In a whole chunk each thread issues its four 16-byte
-// loads before its stores, so a workgroup keeps 16 KiB in flight; the last,
-// partial chunk of a block copies one vector at a time.
-// ---------------------------------------------------------------------------
-constexpr int kCopyThreads = 256;
-constexpr int kCopyVecs = int(kCopyChunkBytes / (16 * kCopyThreads));
-
-__global__ __launch_bounds__(kCopyThreads) void copy_blocks_kernel(CopyArgs a) {
-  const int pair = blockIdx.x / a.chunks;
-  const int chunk = blockIdx.x - pair * a.chunks;
-  const int32_t src = a.mapping[2 * pair];
-  const int32_t dst = a.mapping[2 * pair + 1];
-  if (src < 0 || src >= a.num_blocks || dst < 0 || dst >= a.num_blocks) return;
-  char* pool = a.pools[blockIdx.y];
-  const uint4* from = reinterpret_cast<const uint4*>(pool + int64_t(src) * a.block_bytes);
-  uint4* to = reinterpret_cast<uint4*>(pool + int64_t(dst) * a.block_bytes);
-  const int64_t vecs = a.block_bytes / 16;
-  const int64_t first = int64_t(chunk) * (kCopyThreads * kCopyVecs);
-  if (first + kCopyThreads * kCopyVecs <= vecs) {
-    // a whole chunk (the same branch for the whole workgroup)
-    // four named registers: an array here is turned into LDS by the compiler
-    static_assert(kCopyVecs == 4, "one register per vector below");
-    const int64_t i = first + threadIdx.x;
-    const uint4 v0 = from[i];
-    const uint4 v1 = from[i + kCopyThreads];
-    const uint4 v2 = from[i + 2 * kCopyThreads];
-    const uint4 v3 = from[i + 3 * kCopyThreads];
-    to[i] = v0;
-    to[i + kCopyThreads] = v1;
-    to[i + 2 * kCopyThreads] = v2;
-    to[i + 3 * kCopyThreads] = v3;
-  } else {
-    for (int64_t i = first + threadIdx.x; i < vecs; i += kCopyThreads) to[i] = from[i];
   }
 }
 
@@ -1690,38 +1653,6 @@ int resident_workgroups(const void* kernel, int kernel_id, int threads) {
   return n;
 }
 
-// ---------------------------------------------------------------------------
-// Kernel timing for measurements (pa_profile_start / pa_profile_stop): while
-// it is on, each call launches its attention kernel with a start and a stop
-// event attached to that dispatch, so the pair brackets the kernel alone.
-struct KernelTimer {
-  std::atomic<bool> on{false};
-  std::mutex mu;
-  std::vector<std::pair<hipEvent_t, hipEvent_t>> events;
-};
-KernelTimer& kernel_timer() {
-  static KernelTimer t;
-  return t;
-}
-
-template <typename Kernel, typename... Args>
-void launch_attention(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, Args... args) {
-  KernelTimer& t = kernel_timer();
-  if (t.on.load(std::memory_order_relaxed)) {
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (hipEventCreate(&e0) == hipSuccess && hipEventCreate(&e1) == hipSuccess) {
-      {
-        std::lock_guard<std::mutex> lock(t.mu);
-        t.events.emplace_back(e0, e1);
-      }
-      hipExtLaunchKernelGGL(kernel, grid, block, 0, stream, e0, e1, 0, args...);
-      return;
-    }
-    if (e0) (void)hipEventDestroy(e0);
-  }
-  hipLaunchKernelGGL(kernel, grid, block, 0, stream, args...);
-}
-
 template <int DT, int D, int G>
 hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
   if (args.num_partitions == 0) {
@@ -1740,16 +1671,16 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
       const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 4 + mode, kWave);
       if (W <= 0) return hipErrorInvalidDevice;
       if (mode == 1)
-        launch_attention(decode_stream_kernel<DT, D, G, true, false, false>, dim3(W), dim3(kWave),
+        launch_timed(decode_stream_kernel<DT, D, G, true, false, false>, dim3(W), dim3(kWave),
                          stream, a);
       else if (mode == 2)
-        launch_attention(decode_stream_kernel<DT, D, G, false, true, false>, dim3(W), dim3(kWave),
+        launch_timed(decode_stream_kernel<DT, D, G, false, true, false>, dim3(W), dim3(kWave),
                          stream, a);
       else if (mode == 3)
-        launch_attention(decode_stream_kernel<DT, D, G, false, false, true>, dim3(W), dim3(kWave),
+        launch_timed(decode_stream_kernel<DT, D, G, false, false, true>, dim3(W), dim3(kWave),
                          stream, a);
       else
-        launch_attention(decode_stream_kernel<DT, D, G, false, false, false>, dim3(W), dim3(kWave),
+        launch_timed(decode_stream_kernel<DT, D, G, false, false, false>, dim3(W), dim3(kWave),
                          stream, a);
       hipLaunchKernelGGL((merge_pieces_kernel<DT, D, G>), dim3(W),
                          dim3(MergeShape<G, D>::kThreads), 0, stream, a, W);
@@ -1768,10 +1699,10 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
     const dim3 grid(a.num_partitions, a.num_kv_heads, a.num_seqs);
     // a 16-token tile lies inside one block when the block size is a multiple of 16
     if (a.log2_block >= 4) {
-      launch_attention(decode_partition_kernel<DT, D, G, true>, grid,
+      launch_timed(decode_partition_kernel<DT, D, G, true>, grid,
                        dim3(kWave * kPartitionWaves), stream, a);
     } else {
-      launch_attention(decode_partition_kernel<DT, D, G, false>, grid,
+      launch_timed(decode_partition_kernel<DT, D, G, false>, grid,
                        dim3(kWave * kPartitionWaves), stream, a);
     }
     if (a.num_partitions > 1) {
@@ -1810,6 +1741,11 @@ hipError_t launch_decode_dt(const DecodeArgs& a, int32_t head_dim, int32_t group
 }
 
 }  // namespace
+
+KernelTimer& kernel_timer() {
+  static KernelTimer t;
+  return t;
+}
 
 void profile_start() {
   KernelTimer& t = kernel_timer();
@@ -1851,9 +1787,9 @@ hipError_t launch_prefill_g(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid((a.max_query_len + PrefillShape<G>::kQueries - 1) / PrefillShape<G>::kQueries,
                     a.num_kv_heads, a.num_seqs);
     if (a.log2_block >= 4)
-      launch_attention(prefill_kernel<DT, D, G, true>, grid, dim3(kWave), stream, a);
+      launch_timed(prefill_kernel<DT, D, G, true>, grid, dim3(kWave), stream, a);
     else
-      launch_attention(prefill_kernel<DT, D, G, false>, grid, dim3(kWave), stream, a);
+      launch_timed(prefill_kernel<DT, D, G, false>, grid, dim3(kWave), stream, a);
     return hipGetLastError();
   }
 }
@@ -1899,14 +1835,6 @@ hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream) {
   if (a.num_tokens == 0) return hipSuccess;
   hipLaunchKernelGGL(write_kv_kernel, dim3(a.num_tokens), dim3(256), 0, stream, a);
-  return hipGetLastError();
-}
-
-hipError_t launch_copy_blocks(const CopyArgs& a, int32_t num_pairs, int32_t num_pools,
-                              hipStream_t stream) {
-  if (num_pairs == 0 || num_pools == 0) return hipSuccess;
-  launch_attention(copy_blocks_kernel, dim3(num_pairs * a.chunks, num_pools), dim3(kCopyThreads),
-                   stream, a);
   return hipGetLastError();
 }
 
