@@ -1487,26 +1487,60 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // ---------------------------------------------------------------------------
 // Chunked prefill: causal attention of each sequence's last M tokens (a prompt
 // chunk; a decode token is M = 1).  One wave per (query block, kv head,
-// sequence).  A query block fills the 16 columns of the MFMA operand that
-// holds Q^T: kQueries = 16 / G queries times the G heads of the kv head, so
-// the key and value tiles read for it serve all of them.  Column c is query
-// r = c / G of the block (head c % G) at position T - M + r; key rows after
-// that position get weight zero (its per-lane `live` bound), and the wave
-// streams the tiles up to the block's last position with the decode kernels'
-// tile math and prefetching.
+// sequence).  A query block is kBlocks column blocks; each fills the 16
+// columns of an MFMA operand holding Q^T with 16 / G queries times the G heads
+// of the kv head.  Every key tile the wave loads into registers, and every
+// value tile it stages in LDS, serves all its column blocks, so the tile
+// traffic per matrix-core operation falls by kBlocks.  Column c of block b is
+// query r = b * 16 / G + c / G of the query block (head c % G) at position
+// T - M + r; key rows after that position get weight zero (its per-lane
+// `live` bound), and the wave streams the tiles up to its last position with
+// the decode kernels' tile math and prefetching.  Query blocks are handed out
+// latest first: they attend to the most keys, so they start early.
 // ---------------------------------------------------------------------------
 template <int G>
 struct PrefillShape {
-  static constexpr int kQueries = 16 / G;
-  static constexpr int kCols = kQueries * G;
+  static constexpr int kBlockQueries = 16 / G;          // queries per column block
+  static constexpr int kBlocks = 2;                     // column blocks per wave
+  static constexpr int kQueries = kBlockQueries * kBlocks;
 };
 
+// O^T += V^T . P^T for every column block: each transposed read of the value
+// tile feeds one MFMA per block
+template <int DT, int D, int NB>
+__device__ __forceinline__ void accumulate_blocks(MfmaPv<DT, D, 16> (&tm)[NB], const char* vt) {
+  using TM = MfmaPv<DT, D, 16>;
+  v4i16 pb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int n = 0; n < TM::NT; ++n) tm[b].o[n] *= tm[b].alpha_;
+    pb[b] = pack4<DT>(tm[b].p_);
+  }
+  wave_sync_lds();
+  const int c = tm[0].c;
+  const int row = 4 * tm[0].gq + (c >> 2);
+  const char* rbase = vt + row * TM::kRowBytes + ((c & 1) << 3);
+  const int sw = TM::swz(row);
+#pragma unroll
+  for (int n = 0; n < TM::NT; ++n) {
+    const int chunk = 2 * n + ((c & 3) >> 1);
+    const v4i16 av =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(rbase + ((chunk ^ sw) << 4)));
+#pragma unroll
+    for (int b = 0; b < NB; ++b) tm[b].o[n] = mfma_pv<DT>(av, pb[b], tm[b].o[n]);
+  }
+  wave_sync_lds();
+}
+
 template <int DT, int D, int G, bool kTileInBlock>
-__global__ __launch_bounds__(kWave) void prefill_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, 16>;
   constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
   constexpr int kRowBytes = GE::kRowBytes;
-  constexpr int QB = PrefillShape<G>::kQueries;
+  constexpr int BQ = PrefillShape<G>::kBlockQueries;
+  constexpr int NB = PrefillShape<G>::kBlocks;
+  constexpr int QW = PrefillShape<G>::kQueries;
   using TM = MfmaPv<DT, D, 16>;
   __shared__ __align__(16) char vtile[TM::kScratchBytes];
 
@@ -1516,23 +1550,30 @@ __global__ __launch_bounds__(kWave) void prefill_kernel(DecodeArgs a) {
   const int T = min(max(a.context_lens[seq], 0), a.max_context_len);
   const int row_begin = a.query_start[seq];
   const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
-  const int r0 = blockIdx.x * QB;
+  const int r0 = (gridDim.x - 1 - blockIdx.x) * QW;       // latest query blocks first
   if (r0 >= M) return;
-  const int nq = min(QB, M - r0);
+  const int nq = min(QW, M - r0);
 
-  TM tm;
-  tm.set_lane(lane);
+  TM tm[NB];
   const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
-  const bool col_ok = c < nq * G;
-  const int qr = r0 + (col_ok ? c / G : 0);                 // query row of this column
-  const int head = g * G + (col_ok ? c % G : 0);
-  const int pos = T - M + qr;                               // its position
-  const int64_t out_row = int64_t(row_begin + qr) * a.num_q_heads + head;
-  const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
-                                                     out_row * kRowBytes);
+  bool col_ok[NB];
+  int pos[NB];
+  int64_t out_row[NB];
 #pragma unroll
-  for (int kk = 0; kk < KK; ++kk) tm.qb[kk] = col_ok ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
-  tm.reset();
+  for (int b = 0; b < NB; ++b) {
+    tm[b].set_lane(lane);
+    col_ok[b] = b * BQ + c / G < nq && c < BQ * G;
+    const int qr = r0 + (col_ok[b] ? b * BQ + c / G : 0);   // query row of this column
+    const int head = g * G + (col_ok[b] ? c % G : 0);
+    pos[b] = T - M + qr;                                      // its position
+    out_row[b] = int64_t(row_begin + qr) * a.num_q_heads + head;
+    const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                       out_row[b] * kRowBytes);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      tm[b].qb[kk] = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+    tm[b].reset();
+  }
 
   const int ntiles = (T - M + r0 + nq - 1) / kTileTokens + 1;   // up to the last position
   const int lb = a.log2_block;
@@ -1602,16 +1643,19 @@ __global__ __launch_bounds__(kWave) void prefill_kernel(DecodeArgs a) {
   load_values(0, VR);
   if (ntiles > 1) load_keys(1, KB);
   auto step = [&](int k, KeyRegs<DT, D>& kr) {
-    tm.stage_values(VR, vtile);
+    tm[0].stage_values(VR, vtile);
     if (k + 1 < ntiles) load_values(k + 1, VR);
-    // keys at positions 16k .. pos of this column take part
-    const int live = col_ok ? min(kTileTokens, max(0, pos - k * kTileTokens + 1)) : 0;
-    tm.scores(a, kr, 0, live);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // keys at positions 16k .. pos of this column take part
+      const int live = col_ok[b] ? min(kTileTokens, max(0, pos[b] - k * kTileTokens + 1)) : 0;
+      tm[b].scores(a, kr, 0, live);
+    }
     if (k + 2 < ntiles) {
       if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
       load_keys(k + 2, kr);
     }
-    tm.accumulate(vtile);
+    accumulate_blocks<DT, D, NB>(tm, vtile);
   };
   for (int k = 0; k < ntiles; k += 2) {
     step(k, KA);
@@ -1619,15 +1663,18 @@ __global__ __launch_bounds__(kWave) void prefill_kernel(DecodeArgs a) {
     step(k + 1, KB);
   }
 
-  // column c's sum is spread over its four lanes (gq = 0..3)
-  float l = tm.l_run;
-  l += __shfl_xor(l, 16, kWave);
-  l += __shfl_xor(l, 32, kWave);
-  if (col_ok) {
-    const float inv = 1.0f / l;
 #pragma unroll
-    for (int n = 0; n < TM::NT; ++n)
-      store4<DT>(a.out, out_row * D + 16 * n + 4 * gq, tm.o[n] * inv);
+  for (int b = 0; b < NB; ++b) {
+    // column c's sum is spread over its four lanes (gq = 0..3)
+    float l = tm[b].l_run;
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (col_ok[b]) {
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int n = 0; n < TM::NT; ++n)
+        store4<DT>(a.out, out_row[b] * D + 16 * n + 4 * gq, tm[b].o[n] * inv);
+    }
   }
 }
 
