@@ -1495,15 +1495,73 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // query r = b * 16 / G + c / G of the query block (head c % G) at position
 // T - M + r; key rows after that position get weight zero (its per-lane
 // `live` bound), and the wave streams the tiles up to its last position with
-// the decode kernels' tile math and prefetching.  Query blocks are handed out
-// latest first: they attend to the most keys, so they start early.
+// the decode kernels' tile math and prefetching.
+//
+// Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
+// own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
+// pair after another, so the pair's key and value tiles, read by every one of
+// its query blocks, stay in that XCD's L2.  Within a pair the query blocks are
+// handed out latest first: they attend to the most keys, so they start early.
 // ---------------------------------------------------------------------------
 template <int G>
 struct PrefillShape {
   static constexpr int kBlockQueries = 16 / G;          // queries per column block
-  static constexpr int kBlocks = 2;                     // column blocks per wave
+  static constexpr int kBlocks = kPrefillColumnBlocks;  // column blocks per wave
   static constexpr int kQueries = kBlockQueries * kBlocks;
 };
+
+// The maximum over the four lanes of each column (lanes c, c + 16, c + 32,
+// c + 48): row swaps on the vector ALU rather than permutes through LDS.
+__device__ __forceinline__ float column_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Softmax reference of the prefill: a column keeps its reference m until a
+// tile's maximum exceeds it by more than kRefSlack (log2 units); only then are
+// the wave's sums and outputs rescaled (a wave-uniform branch).  The result is
+// the same softmax: every weight exp2(s - m) stays at most 2^kRefSlack, well
+// inside float32 and bfloat16 range, and the relative precision of the
+// weights does not depend on their scale.
+constexpr float kRefSlack = 8.0f;
+
+template <int DT, int D>
+__device__ __forceinline__ void prefill_scores(MfmaPv<DT, D, 16>& t, const DecodeArgs& a,
+                                               const KeyRegs<DT, D>& r, int live) {
+  using TM = MfmaPv<DT, D, 16>;
+  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < TM::KK; ++kk) sc = mfma_chunk<DT>(r.k[kk], t.qb[kk], sc);
+  float s[4];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s[i] = 4 * t.gq + i < live ? sc[i] * a.scale_log2 : -INFINITY;
+    mx = fmaxf(mx, s[i]);
+  }
+  mx = column_max(mx);
+  if (__builtin_amdgcn_ballot_w64(mx > t.m_run + kRefSlack) != 0) {
+    const float m_new = fmaxf(t.m_run, mx);
+    // a column with nothing so far (m_new = -inf) has nothing to rescale
+    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
+#pragma unroll
+    for (int n = 0; n < TM::NT; ++n) t.o[n] *= alpha;
+    t.l_run *= alpha;
+    t.m_run = m_new;
+  }
+  const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
+  float psum = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    t.p_[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+    psum += t.p_[i];
+  }
+  t.l_run += psum;
+}
 
 // O^T += V^T . P^T for every column block: each transposed read of the value
 // tile feeds one MFMA per block
@@ -1512,11 +1570,7 @@ __device__ __forceinline__ void accumulate_blocks(MfmaPv<DT, D, 16> (&tm)[NB], c
   using TM = MfmaPv<DT, D, 16>;
   v4i16 pb[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int n = 0; n < TM::NT; ++n) tm[b].o[n] *= tm[b].alpha_;
-    pb[b] = pack4<DT>(tm[b].p_);
-  }
+  for (int b = 0; b < NB; ++b) pb[b] = pack4<DT>(tm[b].p_);
   wave_sync_lds();
   const int c = tm[0].c;
   const int row = 4 * tm[0].gq + (c >> 2);
@@ -1544,13 +1598,18 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   using TM = MfmaPv<DT, D, 16>;
   __shared__ __align__(16) char vtile[TM::kScratchBytes];
 
-  const int seq = blockIdx.z;
-  const int g = blockIdx.y;
+  const int nqb = (a.max_query_len - 1) / QW + 1;          // query blocks per pair (>= 1)
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;                         // this XCD's j-th workgroup
+  const int pair = xcd + kXcds * (j / nqb);
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int seq = pair / a.num_kv_heads;
+  const int g = pair - seq * a.num_kv_heads;
   const int lane = threadIdx.x;
   const int T = min(max(a.context_lens[seq], 0), a.max_context_len);
   const int row_begin = a.query_start[seq];
   const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
-  const int r0 = (gridDim.x - 1 - blockIdx.x) * QW;       // latest query blocks first
+  const int r0 = (nqb - 1 - j % nqb) * QW;                 // latest query blocks first
   if (r0 >= M) return;
   const int nq = min(QW, M - r0);
 
@@ -1649,7 +1708,7 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
     for (int b = 0; b < NB; ++b) {
       // keys at positions 16k .. pos of this column take part
       const int live = col_ok[b] ? min(kTileTokens, max(0, pos[b] - k * kTileTokens + 1)) : 0;
-      tm[b].scores(a, kr, 0, live);
+      prefill_scores<DT, D>(tm[b], a, kr, live);
     }
     if (k + 2 < ntiles) {
       if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
@@ -1831,8 +1890,8 @@ hipError_t launch_prefill_g(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (DT == PA_F32) {
     return hipErrorInvalidValue;
   } else {
-    const dim3 grid((a.max_query_len + PrefillShape<G>::kQueries - 1) / PrefillShape<G>::kQueries,
-                    a.num_kv_heads, a.num_seqs);
+    const dim3 grid(static_cast<uint32_t>(
+        prefill_workgroups(a.num_seqs, a.num_kv_heads, G, a.max_query_len)));
     if (a.log2_block >= 4)
       launch_timed(prefill_kernel<DT, D, G, true>, grid, dim3(kWave), stream, a);
     else

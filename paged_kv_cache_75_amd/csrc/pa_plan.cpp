@@ -1,6 +1,8 @@
 // Host-side argument checks and launch planning (no HIP calls).
 #include "pa_plan.h"
 
+#include <climits>
+
 namespace pa {
 
 namespace {
@@ -126,6 +128,8 @@ pa_status check_prefill(int32_t num_seqs, int32_t num_q_heads, const pa_pool_des
   if (max_blocks_per_seq <= 0 && num_seqs > 0) return PA_ERR_INVALID_ARGUMENT;
   if (max_query_len < 0 || max_query_len > max_context_len) return PA_ERR_INVALID_ARGUMENT;
   if (pool->dtype == PA_F32) return PA_ERR_UNSUPPORTED;   // matrix-core tile math only
+  if (prefill_workgroups(num_seqs, pool->num_kv_heads, p.group, max_query_len) > INT32_MAX)
+    return PA_ERR_UNSUPPORTED;                             // one-dimensional grid
   *group = p.group;
   return PA_OK;
 }
