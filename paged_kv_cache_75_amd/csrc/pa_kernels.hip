@@ -1522,67 +1522,103 @@ __device__ __forceinline__ float column_max(float x) {
 }
 
 // Softmax reference of the prefill: a column keeps its reference m until a
-// tile's maximum exceeds it by more than kRefSlack (log2 units); only then are
+// step's maximum exceeds it by more than kRefSlack (log2 units); only then are
 // the wave's sums and outputs rescaled (a wave-uniform branch).  The result is
 // the same softmax: every weight exp2(s - m) stays at most 2^kRefSlack, well
 // inside float32 and bfloat16 range, and the relative precision of the
 // weights does not depend on their scale.
 constexpr float kRefSlack = 8.0f;
 
+// One 16-column block of a prefill wave: Q^T operand, O^T accumulators, the
+// running reference and sum, and the step's weights.
 template <int DT, int D>
-__device__ __forceinline__ void prefill_scores(MfmaPv<DT, D, 16>& t, const DecodeArgs& a,
-                                               const KeyRegs<DT, D>& r, int live) {
-  using TM = MfmaPv<DT, D, 16>;
-  f32x4 sc = {0.0f, 0.0f, 0.0f, 0.0f};
+struct PrefillCols {
+  static constexpr int KK = D / 32;            // 32-element chunks of a query row
+  static constexpr int NT = D / 16;            // 16-row tiles of O^T
+  uint4 qb[KK];
+  f32x4 o[NT];
+  float m_run, l_run;
+  float p[8];                                  // keys 4gq + i of each 16-key half
+};
+
+// A step is 32 keys: two 16-key tiles (halves).  S^T = K . Q^T per half gives
+// lane (gq, c) the scores of keys 4gq .. 4gq+3 of each half for column c;
+// those eight weights are, in that order, the lane's B operand of the
+// 16x16x32 product O^T += V^T . P^T (the contraction over keys may take them
+// in any order, as long as V^T's chunks follow the same order).
+template <int DT, int D>
+__device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const DecodeArgs& a,
+                                                 const KeyRegs<DT, D>& k0,
+                                                 const KeyRegs<DT, D>& k1, int gq, int live0,
+                                                 int live1) {
+  f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-  for (int kk = 0; kk < TM::KK; ++kk) sc = mfma_chunk<DT>(r.k[kk], t.qb[kk], sc);
-  float s[4];
+  for (int kk = 0; kk < PrefillCols<DT, D>::KK; ++kk) {
+    s0 = mfma_chunk<DT>(k0.k[kk], t.qb[kk], s0);
+    s1 = mfma_chunk<DT>(k1.k[kk], t.qb[kk], s1);
+  }
+  float s[8];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[i] = 4 * t.gq + i < live ? sc[i] * a.scale_log2 : -INFINITY;
-    mx = fmaxf(mx, s[i]);
+    s[i] = 4 * gq + i < live0 ? s0[i] * a.scale_log2 : -INFINITY;
+    s[4 + i] = 4 * gq + i < live1 ? s1[i] * a.scale_log2 : -INFINITY;
   }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
   mx = column_max(mx);
   if (__builtin_amdgcn_ballot_w64(mx > t.m_run + kRefSlack) != 0) {
     const float m_new = fmaxf(t.m_run, mx);
     // a column with nothing so far (m_new = -inf) has nothing to rescale
     const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
 #pragma unroll
-    for (int n = 0; n < TM::NT; ++n) t.o[n] *= alpha;
+    for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
     t.l_run *= alpha;
     t.m_run = m_new;
   }
   const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
   float psum = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    t.p_[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-    psum += t.p_[i];
+  for (int i = 0; i < 8; ++i) {
+    t.p[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
+    psum += t.p[i];
   }
   t.l_run += psum;
 }
 
-// O^T += V^T . P^T for every column block: each transposed read of the value
-// tile feeds one MFMA per block
+// O^T += V^T . P^T over a 32-key step for every column block.  The value
+// tile holds the step's 32 rows in LDS (row r at r * row bytes, 16-byte
+// chunks swizzled per row); a transposed read gives lane (gq, c) four keys of
+// one dimension, 4gq .. 4gq+3 of a half, and the read 16 rows further on the
+// same four keys of the second half: together the A operand chunk matching
+// the weights' order.
 template <int DT, int D, int NB>
-__device__ __forceinline__ void accumulate_blocks(MfmaPv<DT, D, 16> (&tm)[NB], const char* vt) {
-  using TM = MfmaPv<DT, D, 16>;
-  v4i16 pb[NB];
+__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const char* vt,
+                                             int gq, int c) {
+  using GE = Geo<DT, D, 16>;
+  constexpr int kRowBytes = GE::kRowBytes;
+  // two four-element halves as one eight-element operand chunk
+  auto join = [](v4i16 lo, v4i16 hi) {
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    return make_uint4(l.x, l.y, h.x, h.y);
+  };
+  uint4 pb[NB];
 #pragma unroll
-  for (int b = 0; b < NB; ++b) pb[b] = pack4<DT>(tm[b].p_);
+  for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
   wave_sync_lds();
-  const int c = tm[0].c;
-  const int row = 4 * tm[0].gq + (c >> 2);
-  const char* rbase = vt + row * TM::kRowBytes + ((c & 1) << 3);
-  const int sw = TM::swz(row);
+  const int row = 4 * gq + (c >> 2);
+  const char* rbase = vt + row * kRowBytes + ((c & 1) << 3);
+  const int sw = MfmaPv<DT, D, 16>::swz(row);
 #pragma unroll
-  for (int n = 0; n < TM::NT; ++n) {
+  for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) {
     const int chunk = 2 * n + ((c & 3) >> 1);
-    const v4i16 av =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(rbase + ((chunk ^ sw) << 4)));
+    const char* at = rbase + ((chunk ^ sw) << 4);
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kRowBytes));
+    const uint4 av = join(lo, hi);
 #pragma unroll
-    for (int b = 0; b < NB; ++b) tm[b].o[n] = mfma_pv<DT>(av, pb[b], tm[b].o[n]);
+    for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
   }
   wave_sync_lds();
 }
@@ -1595,8 +1631,8 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   constexpr int BQ = PrefillShape<G>::kBlockQueries;
   constexpr int NB = PrefillShape<G>::kBlocks;
   constexpr int QW = PrefillShape<G>::kQueries;
-  using TM = MfmaPv<DT, D, 16>;
-  __shared__ __align__(16) char vtile[TM::kScratchBytes];
+  using PC = PrefillCols<DT, D>;
+  __shared__ __align__(16) char vtile[2 * kTileTokens * kRowBytes];   // a step's 32 rows
 
   const int nqb = (a.max_query_len - 1) / QW + 1;          // query blocks per pair (>= 1)
   const int xcd = blockIdx.x % kXcds;
@@ -1613,14 +1649,13 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   if (r0 >= M) return;
   const int nq = min(QW, M - r0);
 
-  TM tm[NB];
+  PC cols[NB];
   const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
   bool col_ok[NB];
   int pos[NB];
   int64_t out_row[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    tm[b].set_lane(lane);
     col_ok[b] = b * BQ + c / G < nq && c < BQ * G;
     const int qr = r0 + (col_ok[b] ? b * BQ + c / G : 0);   // query row of this column
     const int head = g * G + (col_ok[b] ? c % G : 0);
@@ -1630,11 +1665,15 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
                                                        out_row[b] * kRowBytes);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk)
-      tm[b].qb[kk] = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
-    tm[b].reset();
+      cols[b].qb[kk] = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < PC::NT; ++n) cols[b].o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    cols[b].m_run = -INFINITY;
+    cols[b].l_run = 0.0f;
   }
 
   const int ntiles = (T - M + r0 + nq - 1) / kTileTokens + 1;   // up to the last position
+  const int nsteps = (ntiles + 1) / 2;                          // 32-key steps
   const int lb = a.log2_block;
   const int bmask = (1 << lb) - 1;
   const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
@@ -1656,15 +1695,18 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
     const int64_t blk = __builtin_amdgcn_readlane(tbl, k & 63);
     return (blk * blk_rows + head_rows + ((k * kTileTokens) & bmask)) * kRowBytes;
   };
+  // the buffer spans the tile's rows below T only; a tile past the wave's
+  // last position (the second half of its last step) spans none: its table
+  // lane holds another tile's block, and it must read as zeros
   auto rsrc = [&](const char* base, int k) {
+    const int rows = k < ntiles ? min(kTileTokens, T - k * kTileTokens) : 0;
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + tile_byte(k)), 0,
-                                             min(kTileTokens, T - k * kTileTokens) * kRowBytes,
-                                             kBufferDword3);
+                                             rows * kRowBytes, kBufferDword3);
   };
   // blocks smaller than a tile: each lane finds its row's block; rows past
   // T - 1 read row T - 1 (weight zero)
   auto row_of = [&](int t0, int dt) -> int64_t {
-    const int t = t0 + min(dt, T - 1 - t0);
+    const int t = min(t0 + dt, T - 1);
     const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
     return blk * blk_rows + head_rows + (t & bmask);
   };
@@ -1694,45 +1736,68 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
             vbase + row_of(k * kTileTokens, s2 * RPI + rho) * kRowBytes)[chi];
     }
   };
+  auto stage = [&](const ValRegs<DT, D>& r, char* vt) {
+#pragma unroll
+    for (int s2 = 0; s2 < VS; ++s2) {
+      const int row = s2 * RPI + rho;
+      *reinterpret_cast<uint4*>(vt + row * kRowBytes +
+                                ((chi ^ MfmaPv<DT, D, 16>::swz(row)) << 4)) = r.v[s2];
+    }
+  };
 
+  struct StepKeys {
+    KeyRegs<DT, D> h[2];
+  };
   if constexpr (kTileInBlock) load_tbl(0);
-  KeyRegs<DT, D> KA, KB;
-  ValRegs<DT, D> VR;
-  load_keys(0, KA);
-  load_values(0, VR);
-  if (ntiles > 1) load_keys(1, KB);
-  auto step = [&](int k, KeyRegs<DT, D>& kr) {
-    tm[0].stage_values(VR, vtile);
-    if (k + 1 < ntiles) load_values(k + 1, VR);
+  StepKeys KA, KB;
+  ValRegs<DT, D> V0, V1;
+  load_keys(0, KA.h[0]);
+  load_keys(1, KA.h[1]);
+  load_values(0, V0);
+  load_values(1, V1);
+  if (nsteps > 1) {
+    load_keys(2, KB.h[0]);
+    load_keys(3, KB.h[1]);
+  }
+  auto step = [&](int st, StepKeys& kr) {
+    stage(V0, vtile);
+    stage(V1, vtile + kTileTokens * kRowBytes);
+    if (st + 1 < nsteps) {
+      load_values(2 * st + 2, V0);
+      load_values(2 * st + 3, V1);
+    }
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      // keys at positions 16k .. pos of this column take part
-      const int live = col_ok[b] ? min(kTileTokens, max(0, pos[b] - k * kTileTokens + 1)) : 0;
-      prefill_scores<DT, D>(tm[b], a, kr, live);
+      // keys at positions 32 st .. pos of this column take part
+      const int before = col_ok[b] ? pos[b] - 2 * st * kTileTokens + 1 : 0;
+      prefill_scores32<DT, D>(cols[b], a, kr.h[0], kr.h[1], gq,
+                              min(kTileTokens, max(0, before)),
+                              min(kTileTokens, max(0, before - kTileTokens)));
     }
-    if (k + 2 < ntiles) {
-      if (kTileInBlock && ((k + 2) & 63) == 0) load_tbl((k + 2) >> 6);
-      load_keys(k + 2, kr);
+    if (st + 2 < nsteps) {
+      if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
+      load_keys(2 * st + 4, kr.h[0]);
+      load_keys(2 * st + 5, kr.h[1]);
     }
-    accumulate_blocks<DT, D, NB>(tm, vtile);
+    accumulate32<DT, D, NB>(cols, vtile, gq, c);
   };
-  for (int k = 0; k < ntiles; k += 2) {
-    step(k, KA);
-    if (k + 1 >= ntiles) break;
-    step(k + 1, KB);
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, KA);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, KB);
   }
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     // column c's sum is spread over its four lanes (gq = 0..3)
-    float l = tm[b].l_run;
+    float l = cols[b].l_run;
     l += __shfl_xor(l, 16, kWave);
     l += __shfl_xor(l, 32, kWave);
     if (col_ok[b]) {
       const float inv = 1.0f / l;
 #pragma unroll
-      for (int n = 0; n < TM::NT; ++n)
-        store4<DT>(a.out, out_row[b] * D + 16 * n + 4 * gq, tm[b].o[n] * inv);
+      for (int n = 0; n < PC::NT; ++n)
+        store4<DT>(a.out, out_row[b] * D + 16 * n + 4 * gq, cols[b].o[n] * inv);
     }
   }
 }
