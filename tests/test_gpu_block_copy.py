@@ -80,6 +80,41 @@ def test_copy_blocks_parity(case):
         assert np.array_equal(_bytes(got), _bytes(w)), f"pool {p} differs"
 
 
+def test_copy_blocks_full_size():
+    """The bench's launch: 256 pairs in all 64 pools of Llama-3-8B ([2048][8][16]
+    [128] bf16, 4 GiB).  Every pool is checked on the device against a copy
+    of its sources taken before the launch; two pools are also checked whole
+    against the oracle's copy on the host."""
+    import torch
+    from paged_kv_cache_75_amd import PoolSet, pa_copy_blocks
+    say("[copy] full size: 64 pools x 2048 blocks, 256 pairs")
+    rng = np.random.default_rng(3100)
+    nb = 2048
+    g = torch.Generator(device=DEV)
+    g.manual_seed(3100)
+    pools = [torch.empty((nb, 8, 16, 128), dtype=torch.bfloat16, device=DEV) for _ in range(64)]
+    for p in pools:
+        p.normal_(generator=g)
+    pairs = _pairs(rng, nb, 256)
+    mapping = torch.tensor(pairs, dtype=torch.int32, device=DEV)
+    src = mapping[:, 0].long()
+    dst = mapping[:, 1].long()
+    before = [pools[i][src].clone() for i in range(64)]
+    host = {i: to_host(pools[i], "bf16") for i in (0, 63)}
+    untouched = torch.ones(nb, dtype=torch.bool, device=DEV)
+    untouched[dst] = False
+    rest = [pools[i][untouched].clone() for i in (5, 40)]
+    pa_copy_blocks(PoolSet(pools), mapping)
+    _sync()
+    for i in range(64):
+        assert torch.equal(pools[i][dst], before[i]), f"pool {i}: copied blocks differ"
+    for i, r in zip((5, 40), rest):
+        assert torch.equal(pools[i][untouched], r), f"pool {i}: blocks outside the pairs changed"
+    for i, h in host.items():
+        (want,) = bm.copy_blocks([h], pairs)
+        assert np.array_equal(_bytes(to_host(pools[i], "bf16")), _bytes(want)), f"pool {i}"
+
+
 def test_copy_blocks_no_pairs_is_a_noop():
     import torch
     from paged_kv_cache_75_amd import pa_copy_blocks
@@ -227,3 +262,38 @@ def test_copy_on_write_run():
     r.fork(4, 5)
     assert r.step([4, 5, 0], "step 5 (copy-on-write after a prefix hit)") == 1
     assert r.step([5, 4, 3, 0], "step 6") == 0
+
+
+def test_copy_on_write_random_run():
+    """Twenty steps of random forks, frees and prompts with shared prefixes
+    over 24 sequences and a tight pool; every step compared with the oracle's
+    run (outputs to the bf16 bars, pools bit for bit)."""
+    say("[cow] random run")
+    r = Run(seed=2200, nb=160, max_blocks=12)
+    rng = np.random.default_rng(2201)
+    base = [int(t) for t in rng.integers(0, 1000, 70)]
+    live, next_id, copies = [], 0, 0
+    for _ in range(4):
+        n = int(rng.integers(20, 70))
+        r.admit(next_id, base[:n] + [int(t) for t in rng.integers(0, 1000, int(rng.integers(1, 20)))],
+                kv_from=0 if next_id else None)
+        live.append(next_id)
+        next_id += 1
+    for step in range(20):
+        act = rng.random()
+        if act < 0.3 and len(live) < 24:
+            r.fork(live[int(rng.integers(len(live)))], next_id)
+            live.append(next_id)
+            next_id += 1
+        elif act < 0.4 and len(live) > 3:
+            gone = live.pop(int(rng.integers(len(live))))
+            r.lib.free_seq(gone)
+            r.ref.free_seq(gone)
+        elif act < 0.5 and len(live) < 24:
+            n = int(rng.integers(20, 70))
+            r.admit(next_id, base[:n] + [int(t) for t in rng.integers(0, 1000, 5)], kv_from=0)
+            live.append(next_id)
+            next_id += 1
+        seqs = [s for s in live if len(r.tokens[s]) < 12 * 16]
+        copies += r.step(seqs, f"random step {step} ({len(seqs)} seqs)")
+    assert copies > 0
