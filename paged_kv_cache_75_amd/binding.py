@@ -169,6 +169,10 @@ def _stream(stream):
 
 
 def _check(t, name, dtype=None, dim=None, device=None):
+    # the kernels dereference every pointer on the GPU: a host tensor would
+    # hand them host addresses
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if dtype is not None and t.dtype != dtype:
@@ -179,10 +183,21 @@ def _check(t, name, dtype=None, dim=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
+def _on_current_device(t, name):
+    """Work is enqueued on the current device's stream: the tensors must be
+    there."""
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got one on {t.device}")
+    cur = _torch().cuda.current_device()
+    if t.device.index is not None and t.device.index != cur:
+        raise ValueError(f"{name} is on {t.device} but the current device is cuda:{cur}")
+
+
 def pa_write_kv(k, v, slot_mapping, k_pool, v_pool, stream=None) -> None:
     """Copy k[n], v[n] ([num_tokens][Hkv][D]) into slot slot_mapping[n] of the
     pools; negative slots are skipped."""
     torch = _torch()
+    _on_current_device(k_pool, "k_pool")
     desc = pool_desc(k_pool)
     dev = k_pool.device
     for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool"), (k, "k"), (v, "v")):
@@ -205,6 +220,7 @@ def pa_write_kv_fp8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale, stream
     """pa_write_kv into FP8 (E4M3) pools: each row of k, v is stored as
     codes of x / scale."""
     torch = _torch()
+    _on_current_device(k_pool, "k_pool")
     desc = fp8_pool_desc(k_pool, k)
     dev = k_pool.device
     for t, n in ((k_pool, "k_pool"), (v_pool, "v_pool")):
@@ -229,6 +245,7 @@ def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale,
                   out=None, max_context_len=None, workspace=None, stream=None):
     """pa_decode over FP8 (E4M3) pools with per-pool scales."""
     torch = _torch()
+    _on_current_device(k_pool, "k_pool")
     desc = fp8_pool_desc(k_pool, q)
     dev = k_pool.device
     _check(k_pool, "k_pool", dtype=torch.uint8, device=dev)
@@ -299,6 +316,7 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
     query_start[i] .. query_start[i+1]-1 belong to sequence i.  The host
     bounds are read from the device when omitted (a synchronizing copy)."""
     torch = _torch()
+    _on_current_device(k_pool, "k_pool")
     desc = pool_desc(k_pool)
     dev = k_pool.device
     _check(k_pool, "k_pool")
@@ -347,6 +365,7 @@ def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens
 def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, out,
             max_context_len, workspace, partition_tokens, stream, window=None):
     torch = _torch()
+    _on_current_device(k_pool, "k_pool")
     desc = pool_desc(k_pool)
     dev = k_pool.device
     _check(k_pool, "k_pool")
@@ -403,9 +422,11 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
 # block copy (copy-on-write) and the host block manager
 # ---------------------------------------------------------------------------
 class PoolSet:
-    """Pools for pa_copy_blocks, checked once: tensors of one shape and dtype
-    on one device, axis 0 the block.  Keeps the C array of their pointers, so
-    a step that copies blocks in every layer's pools pays no per-pool work."""
+    """Pools for pa_copy_blocks, checked once: GPU tensors of one shape and
+    dtype on one device, axis 0 the block.  Keeps the C array of their
+    pointers, so a step that copies blocks in every layer's pools pays no
+    per-pool work.  The pointers are taken here: the tensors' storage must
+    not be resized or replaced while the set is in use."""
 
     def __init__(self, pools):
         pools = list(pools)
@@ -435,6 +456,7 @@ def pa_copy_blocks(pools, block_mapping, stream=None) -> None:
     pool (a PoolSet, or a list of tensors of one shape and dtype)."""
     torch = _torch()
     ps = pools if isinstance(pools, PoolSet) else PoolSet(pools)
+    _on_current_device(ps.pools[0], "pools")
     _check(block_mapping, "block_mapping", dtype=torch.int32, device=ps.device)
     if block_mapping.dim() != 2 or block_mapping.shape[1] != 2:
         raise ValueError("block_mapping must be [num_pairs][2]")

@@ -1,0 +1,38 @@
+"""The Python binding's own checks, on the CPU: every wrapper refuses host
+tensors before anything reaches the library (the kernels would dereference
+host addresses on the GPU), and shape / dtype mistakes are caught there."""
+import pytest
+import torch
+
+from paged_kv_cache_75_amd import binding as B
+
+
+def _pool(dtype=torch.bfloat16, nb=4, hkv=2, bs=16, d=128):
+    return torch.zeros((nb, hkv, bs, d), dtype=dtype)
+
+
+def test_host_tensors_are_refused_everywhere():
+    kp, vp = _pool(), _pool()
+    q = torch.zeros((2, 4, 128), dtype=torch.bfloat16)
+    bt = torch.zeros((2, 4), dtype=torch.int32)
+    cl = torch.ones(2, dtype=torch.int32)
+    nk = torch.zeros((2, 2, 128), dtype=torch.bfloat16)
+    calls = {
+        "pa_write_kv": lambda: B.pa_write_kv(nk, nk, cl, kp, vp),
+        "pa_decode": lambda: B.pa_decode(q, kp, vp, bt, cl, 0.1, max_context_len=1),
+        "pa_decode_sliding": lambda: B.pa_decode_sliding(q, kp, vp, bt, cl, 0.1, 8,
+                                                         max_context_len=1),
+        "pa_append_decode": lambda: B.pa_append_decode(q, nk, nk, kp, vp, bt, cl, 0.1,
+                                                       max_context_len=1),
+        "pa_prefill": lambda: B.pa_prefill(q, kp, vp, bt, cl, torch.tensor([0, 1, 2], dtype=torch.int32),
+                                           0.1, max_context_len=1, max_query_len=1),
+        "pa_write_kv_fp8": lambda: B.pa_write_kv_fp8(nk, nk, cl, _pool(torch.uint8),
+                                                     _pool(torch.uint8), 1.0, 1.0),
+        "pa_decode_fp8": lambda: B.pa_decode_fp8(q, _pool(torch.uint8), _pool(torch.uint8), bt,
+                                                 cl, 0.1, 1.0, 1.0, max_context_len=1),
+        "pa_copy_blocks": lambda: B.pa_copy_blocks([kp, vp], torch.zeros((1, 2), dtype=torch.int32)),
+        "PoolSet": lambda: B.PoolSet([kp, vp]),
+    }
+    for name, call in calls.items():
+        with pytest.raises(ValueError, match="GPU tensor"):
+            call()
