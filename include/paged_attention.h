@@ -51,7 +51,7 @@ extern "C" {
 typedef enum pa_status {
   PA_OK = 0,
   PA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative or inconsistent size */
-  PA_ERR_UNSUPPORTED = 2,        /* a valid shape this build does not handle   */
+  PA_ERR_UNSUPPORTED = 2,        /* a valid shape the library does not handle */
   PA_ERR_WORKSPACE_TOO_SMALL = 3,
   PA_ERR_HIP = 4,                /* a HIP runtime call or a launch failed      */
   PA_ERR_OUT_OF_BLOCKS = 5,      /* block manager: not enough free blocks      */
