@@ -38,6 +38,10 @@
  *     get a hash is registered under it (found by later prompts).
  *   - Prefix match: the longest run of leading full prompt blocks whose
  *     hashes are registered, leaving at least one prompt token unmatched.
+ *     A prompt's full blocks are registered when it is admitted, before its
+ *     KV is computed: a request that hits them must not read them before
+ *     the prefill that writes them has run (e.g. admit it in a later step,
+ *     or order its attention after that prefill on the stream).
  *   - Free queue: block ids ascending at creation.  Taking a block pops the
  *     head and drops the block's hash; a block whose count drops to zero
  *     joins the tail; a freed sequence releases its blocks last block first.
