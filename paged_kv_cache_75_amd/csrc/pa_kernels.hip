@@ -1839,7 +1839,23 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
           : mode == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, true, false>)
           : mode == 3 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, true>)
                       : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, false>);
-      const int W = resident_workgroups(k, ((DT * 1000 + D) * 100 + G) * 4 + mode, kWave);
+      // The plain, appending and sliding-window variants split the work the
+      // same way, so their results agree bit for bit (pa_append_decode equals
+      // pa_write_kv + pa_decode): they share one workgroup count, the
+      // smallest any of them keeps resident.
+      const int key = ((DT * 1000 + D) * 100 + G) * 4;
+      int W = resident_workgroups(k, key + mode, kWave);
+      if (mode != 3) {
+        W = std::min({resident_workgroups(reinterpret_cast<const void*>(
+                                              &decode_stream_kernel<DT, D, G, false, false, false>),
+                                          key + 0, kWave),
+                      resident_workgroups(reinterpret_cast<const void*>(
+                                              &decode_stream_kernel<DT, D, G, true, false, false>),
+                                          key + 1, kWave),
+                      resident_workgroups(reinterpret_cast<const void*>(
+                                              &decode_stream_kernel<DT, D, G, false, true, false>),
+                                          key + 2, kWave)});
+      }
       if (W <= 0) return hipErrorInvalidDevice;
       if (mode == 1)
         launch_timed(decode_stream_kernel<DT, D, G, true, false, false>, dim3(W), dim3(kWave),
