@@ -296,6 +296,53 @@ pa_status pa_copy_blocks(void* const* pools, int32_t num_pools, int32_t num_bloc
                          void* stream);
 
 /*
+ * pa_check_inputs -- flag the device-side contract violations of the arrays a
+ * write or decode call reads.  The kernels stay inside the pools whatever
+ * these arrays hold (they skip or clamp), but silently; this call reports.
+ * It never reads the pools.  The rules are those of the slot and table
+ * definitions (vLLM-design page, "How is vLLM's KV cache paged?": one slot per
+ * new token, slot = block * B + offset; "What is the essence of vLLM's
+ * PagedAttention?": a sequence's table names the blocks of its first T tokens).
+ *
+ *   slot_mapping, num_tokens      as pa_write_kv (NULL / 0: not checked).
+ *   block_tables, max_blocks_per_seq, context_lens, num_seqs, max_context_len
+ *                                 as pa_decode (NULL / 0: not checked).
+ *   pool                          the pool the arrays address.
+ *   report        DEVICE int32 [4], written: [0] the number of violations;
+ *                 [1] the kind of the first one, [2] its index, [3] its value
+ *                 (all 0 when there is none).  Kinds, in the order "first"
+ *                 follows (then by index):
+ *                   PA_CHECK_SLOT_RANGE  slot_mapping[n] >= num_blocks * B
+ *                                        (index n, value the slot);
+ *                   PA_CHECK_SLOT_DUP    a live slot used by more than one
+ *                                        token, every such token counted
+ *                                        (index n, value the slot);
+ *                   PA_CHECK_LENGTH      context_lens[i] outside
+ *                                        [0, max_context_len] (index i);
+ *                   PA_CHECK_TABLE       block_tables[i][j] outside
+ *                                        [0, num_blocks) for j < ceil(T_i/B),
+ *                                        T_i clamped as the kernels do
+ *                                        (index i * max_blocks_per_seq + j).
+ *   scratch       DEVICE buffer of pa_check_scratch_bytes(pool) bytes for the
+ *                 duplicate test (two bits per slot); NULL skips that test.
+ *
+ * Work is enqueued on `stream` like the other calls; read `report` after the
+ * stream reaches that point.  Invalid scalars return an error and enqueue
+ * nothing.
+ */
+enum {
+  PA_CHECK_SLOT_RANGE = 1,
+  PA_CHECK_SLOT_DUP = 2,
+  PA_CHECK_LENGTH = 3,
+  PA_CHECK_TABLE = 4
+};
+size_t pa_check_scratch_bytes(const pa_pool_desc* pool);
+pa_status pa_check_inputs(const int32_t* slot_mapping, int32_t num_tokens,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                          const pa_pool_desc* pool, int32_t* report, void* scratch, void* stream);
+
+/*
  * pa_profile_start / pa_profile_stop -- kernel timing for measurements; not
  * needed to compute anything.  Between the two calls, every pa_decode,
  * pa_append_decode, pa_decode_sliding and pa_prefill call launches its

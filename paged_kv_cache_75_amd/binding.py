@@ -28,6 +28,8 @@ PA_ERR_HOST_MEMORY = 6
 
 PA_F32, PA_F16, PA_BF16 = 0, 1, 2
 
+PA_CHECK_SLOT_RANGE, PA_CHECK_SLOT_DUP, PA_CHECK_LENGTH, PA_CHECK_TABLE = 1, 2, 3, 4
+
 
 class PaError(RuntimeError):
     def __init__(self, status: int, where: str):
@@ -85,6 +87,8 @@ def lib():
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
         "pa_status_string": ([c_int], ctypes.c_char_p),
+        "pa_check_scratch_bytes": ([desc], sz),
+        "pa_check_inputs": ([vp, i32, vp, i32, vp, i32, i32, desc, vp, vp, vp], c_int),
         "pa_copy_blocks": ([ctypes.POINTER(vp), i32, i32, ctypes.c_int64, vp, i32, vp], c_int),
         "pa_bm_create": ([i32, i32, i32, ctypes.POINTER(vp)], c_int),
         "pa_bm_destroy": ([vp], None),
@@ -589,3 +593,49 @@ class BlockManager:
         st = lib().pa_bm_free_queue(self._h, out.ctypes.data, self.num_blocks, ctypes.byref(n))
         self._raise(st, "pa_bm_free_queue")
         return [int(b) for b in out[:n.value]]
+
+
+# ---------------------------------------------------------------------------
+# contract check of the device arrays
+# ---------------------------------------------------------------------------
+def pa_check_inputs(k_pool, slot_mapping=None, block_tables=None, context_lens=None,
+                    max_context_len=None, duplicates: bool = True, stream=None):
+    """Check the arrays a write or decode call would read against the pool
+    k_pool ([num_blocks][Hkv][B][D], any element type).  Returns (count,
+    kind, index, value) of the violations, kind/index/value those of the
+    first (0s when there is none).  Synchronizes the stream to read them."""
+    torch = _torch()
+    _on_current_device(k_pool, "k_pool")
+    if k_pool.dim() != 4:
+        raise ValueError("pools are [num_blocks][num_kv_heads][block_size][head_dim]")
+    nb, hkv, bs, d = (int(x) for x in k_pool.shape)
+    desc = pa_pool_desc(nb, bs, hkv, d, PA_BF16)     # the element type plays no part here
+    dev = k_pool.device
+    n_tok, n_seq, mb = 0, 0, 0
+    if slot_mapping is not None:
+        _check(slot_mapping, "slot_mapping", dtype=torch.int32, dim=1, device=dev)
+        n_tok = int(slot_mapping.shape[0])
+    if block_tables is not None or context_lens is not None:
+        if block_tables is None or context_lens is None:
+            raise ValueError("block_tables and context_lens go together")
+        _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+        _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+        n_seq, mb = int(block_tables.shape[0]), int(block_tables.shape[1])
+        if int(context_lens.shape[0]) != n_seq:
+            raise ValueError("context_lens rows must equal block_tables rows")
+        if max_context_len is None:
+            max_context_len = mb * bs
+    report = torch.zeros(4, dtype=torch.int32, device=dev)
+    scratch = None
+    if duplicates and n_tok:
+        scratch = torch.empty(max(int(lib().pa_check_scratch_bytes(ctypes.byref(desc))), 4),
+                              dtype=torch.uint8, device=dev)
+    st = lib().pa_check_inputs(slot_mapping.data_ptr() if n_tok else None, n_tok,
+                               block_tables.data_ptr() if n_seq else None, mb,
+                               context_lens.data_ptr() if n_seq else None, n_seq,
+                               int(max_context_len or 0), ctypes.byref(desc), report.data_ptr(),
+                               scratch.data_ptr() if scratch is not None else None,
+                               _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_check_inputs")
+    return tuple(int(x) for x in report.cpu().tolist())

@@ -61,6 +61,52 @@ pa_status pa_copy_blocks(void* const* pools, int32_t num_pools, int32_t num_bloc
   return PA_OK;
 }
 
+size_t pa_check_scratch_bytes(const pa_pool_desc* pool) {
+  if (pa::check_pool(pool) != PA_OK) return 0;
+  const int64_t slots = int64_t(pool->num_blocks) * pool->block_size;
+  return size_t((slots + 31) / 32) * 2 * sizeof(uint32_t);
+}
+
+pa_status pa_check_inputs(const int32_t* slot_mapping, int32_t num_tokens,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, int32_t num_seqs, int32_t max_context_len,
+                          const pa_pool_desc* pool, int32_t* report, void* scratch,
+                          void* stream) {
+  if (pa::check_pool(pool) != PA_OK || !report) return PA_ERR_INVALID_ARGUMENT;
+  if (reinterpret_cast<uintptr_t>(report) % 8 != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (scratch && reinterpret_cast<uintptr_t>(scratch) % 4 != 0) return PA_ERR_INVALID_ARGUMENT;
+  if (num_tokens < 0 || (num_tokens > 0 && !slot_mapping)) return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs < 0) return PA_ERR_INVALID_ARGUMENT;
+  if (num_seqs > 0) {
+    if (!block_tables || !context_lens || max_blocks_per_seq <= 0 || max_context_len < 0)
+      return PA_ERR_INVALID_ARGUMENT;
+    if (int64_t(max_context_len) > int64_t(max_blocks_per_seq) * pool->block_size)
+      return PA_ERR_INVALID_ARGUMENT;
+    if (int64_t(num_seqs) * max_blocks_per_seq > INT32_MAX) return PA_ERR_UNSUPPORTED;
+  }
+  pa::CheckArgs a{};
+  a.slots = num_tokens > 0 ? slot_mapping : nullptr;
+  a.tables = num_seqs > 0 ? block_tables : nullptr;
+  a.lens = num_seqs > 0 ? context_lens : nullptr;
+  a.report = report;
+  a.num_slots = int64_t(pool->num_blocks) * pool->block_size;
+  a.bitmap_words = (a.num_slots + 31) / 32;
+  if (scratch) {
+    a.seen = static_cast<uint32_t*>(scratch);
+    a.dup = a.seen + a.bitmap_words;
+  }
+  a.num_tokens = num_tokens;
+  a.num_seqs = num_seqs;
+  a.max_blocks = max_blocks_per_seq;
+  a.max_len = max_context_len;
+  a.num_blocks = pool->num_blocks;
+  int32_t lb = 0;
+  while ((1 << lb) < pool->block_size) ++lb;
+  a.log2_block = lb;
+  return pa::launch_check(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PA_OK
+                                                                             : PA_ERR_HIP;
+}
+
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
                                  const pa_pool_desc* pool, int32_t max_context_len,
                                  int32_t partition_tokens) {

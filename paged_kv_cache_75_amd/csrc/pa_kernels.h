@@ -91,6 +91,26 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int32_t num_pairs, int32_t num_
 hipError_t launch_write_kv_fp8(const WriteArgs& a, int32_t dtype, float k_scale, float v_scale,
                                hipStream_t stream);
 
+// Contract check of the device arrays (pa_check_inputs).  bitmap_words: 32-bit
+// words of each of the two slot bitmaps (seen, duplicated) in the scratch.
+struct CheckArgs {
+  const int32_t* slots;
+  const int32_t* tables;
+  const int32_t* lens;
+  int32_t* report;             // [0] count, [2..3] the first violation's key, then kind/index/value
+  uint32_t* seen;              // nullptr: no duplicate test
+  uint32_t* dup;
+  int64_t num_slots;           // num_blocks * block_size
+  int64_t bitmap_words;
+  int32_t num_tokens;
+  int32_t num_seqs;
+  int32_t max_blocks;
+  int32_t max_len;
+  int32_t num_blocks;
+  int32_t log2_block;
+};
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
+
 // Chunked prefill (16-bit pools): causal attention of each sequence's last
 // M_i tokens; group as planned.
 hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, int32_t group,

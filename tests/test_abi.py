@@ -16,7 +16,7 @@ def test_exports_every_declared_function():
     assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding", "pa_prefill",
             "pa_write_kv_fp8", "pa_decode_fp8", "pa_copy_blocks", "pa_bm_create",
             "pa_bm_allocate", "pa_bm_append", "pa_bm_fork", "pa_bm_free", "pa_bm_tables",
-            "pa_sha256", "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
+            "pa_sha256", "pa_check_inputs", "pa_check_scratch_bytes", "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
             "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
@@ -242,3 +242,36 @@ def _copy(pools=(FAKE, FAKE), num_pools=None, nb=64, bb=32768, mapping=FAKE, n=4
 ])
 def test_copy_blocks_validation(kw, want):
     assert _copy(**kw) == want
+
+
+def _check_call(slots=FAKE, ntok=4, tables=FAKE, mb=8, lens=FAKE, nseq=2, maxlen=100, d=True,
+                report=FAKE, scratch=FAKE):
+    pd = desc() if d else None
+    return B.lib().pa_check_inputs(slots, ntok, tables, mb, lens, nseq, maxlen,
+                                   ctypes.byref(pd) if pd is not None else None, report, scratch,
+                                   None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(report=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(report=FAKE + 4), B.PA_ERR_INVALID_ARGUMENT),      # not 8-byte aligned
+    (dict(scratch=FAKE + 2), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(d=False), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(ntok=-1), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(slots=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(nseq=-1), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(tables=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(lens=None), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(mb=0), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(maxlen=8 * 16 + 1), B.PA_ERR_INVALID_ARGUMENT),   # beyond max_blocks_per_seq * B
+    (dict(maxlen=-1), B.PA_ERR_INVALID_ARGUMENT),
+    (dict(nseq=70000, mb=40000, maxlen=16), B.PA_ERR_UNSUPPORTED),
+])
+def test_check_inputs_validation(kw, want):
+    assert _check_call(**kw) == want
+
+
+def test_check_scratch_bytes():
+    d = desc(nb=64, bs=16)
+    assert B.lib().pa_check_scratch_bytes(ctypes.byref(d)) == 2 * 4 * 32    # 1024 slots, 2 bitmaps
+    assert B.lib().pa_check_scratch_bytes(None) == 0
