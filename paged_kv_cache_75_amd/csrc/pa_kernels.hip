@@ -1500,8 +1500,11 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
 // own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
 // pair after another, so the pair's key and value tiles, read by every one of
-// its query blocks, stay in that XCD's L2.  Within a pair the query blocks are
-// handed out latest first: they attend to the most keys, so they start early.
+// its query blocks, stay in that XCD's L2.  Pairs are handed out longest
+// sequence first (up to kWave sequences; beyond that in index order), and
+// within a pair the latest query blocks first: the waves with the most keys
+// start early instead of forming a tail.  Which workgroup runs a (pair, query
+// block) does not change its arithmetic, so the results do not depend on it.
 // ---------------------------------------------------------------------------
 template <int G>
 struct PrefillShape {
@@ -1509,6 +1512,32 @@ struct PrefillShape {
   static constexpr int kBlocks = kPrefillColumnBlocks;  // column blocks per wave
   static constexpr int kQueries = kBlockQueries * kBlocks;
 };
+
+// The sequence of rank k when sequences are ordered by clamped length,
+// longest first, equal lengths by index (num_seqs <= kWave: lane s holds
+// sequence s's length; every workgroup derives the same order).  Binary search
+// for the length v of rank k -- the largest v with more than k lengths >= v --
+// then the (k - #{lengths > v})-th sequence of length v.
+__device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int k, int& len) {
+  const int lane = threadIdx.x;
+  const int key =
+      lane < a.num_seqs ? min(max(a.context_lens[lane], 0), a.max_context_len) : -1;
+  uint32_t lo = 0, hi = uint32_t(a.max_context_len) + 1;   // count(lo) > k >= count(hi)
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (__popcll(__builtin_amdgcn_ballot_w64(key >= int(mid))) > k) lo = mid;
+    else hi = mid;
+  }
+  const int v = int(lo);
+  const int m = k - __popcll(__builtin_amdgcn_ballot_w64(key > v));
+  const uint64_t eq = __builtin_amdgcn_ballot_w64(key == v);
+  const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(eq >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(uint32_t(eq), 0));
+  const int s = __ffsll(static_cast<long long>(
+                    __builtin_amdgcn_ballot_w64(key == v && below == m))) - 1;
+  len = v;
+  return s;
+}
 
 // The maximum over the four lanes of each column (lanes c, c + 16, c + 32,
 // c + 48): row swaps on the vector ALU rather than permutes through LDS.
@@ -1637,12 +1666,18 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   const int nqb = (a.max_query_len - 1) / QW + 1;          // query blocks per pair (>= 1)
   const int xcd = blockIdx.x % kXcds;
   const int j = blockIdx.x / kXcds;                         // this XCD's j-th workgroup
-  const int pair = xcd + kXcds * (j / nqb);
+  const int pair = xcd + kXcds * (j / nqb);                 // pair rank
   if (pair >= a.num_seqs * a.num_kv_heads) return;
-  const int seq = pair / a.num_kv_heads;
-  const int g = pair - seq * a.num_kv_heads;
+  const int rank = pair / a.num_kv_heads;
+  const int g = pair - rank * a.num_kv_heads;
   const int lane = threadIdx.x;
-  const int T = min(max(a.context_lens[seq], 0), a.max_context_len);
+  int T, seq;
+  if (a.num_seqs <= kWave) {
+    seq = seq_of_rank(a, rank, T);
+  } else {
+    seq = rank;
+    T = min(max(a.context_lens[seq], 0), a.max_context_len);
+  }
   const int row_begin = a.query_start[seq];
   const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
   const int r0 = (nqb - 1 - j % nqb) * QW;                 // latest query blocks first
