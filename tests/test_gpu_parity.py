@@ -472,6 +472,19 @@ def test_prefill_mixed_batch(dtype, block_size, group, head_dim):
     _prefill_case(w, mq, 1900 + group, f"{dtype} B={block_size} G={group} D={head_dim}")
 
 
+@pytest.mark.parametrize("num_seqs", [64, 65])
+def test_prefill_order_with_ties(num_seqs):
+    """Pairs are handed out longest sequence first for up to 64 sequences
+    (index order beyond): a batch of many equal lengths, empty sequences and
+    sequences with no query rows must still have every row computed once."""
+    rng = np.random.default_rng(2100 + num_seqs)
+    lens = [int(x) for x in rng.choice([0, 1, 17, 40, 40, 40, 96, 96], size=num_seqs)]
+    mq = [0 if T == 0 else int(rng.choice([0, 1, min(T, 8), T])) for T in lens]
+    w = workloads.random_paged("prefill-order", "bf16", 8, 2, 64, 16, lens,
+                               seed=2200 + num_seqs, spare_frac=0.1)
+    _prefill_case(w, mq, 2300 + num_seqs, f"order n={num_seqs}")
+
+
 def test_prefill_full_size():
     """Sixteen Llama-3-8B sequences, each a 512-token chunk at the end of a
     lognormal context (the prefill bench's batch); four sequences checked
