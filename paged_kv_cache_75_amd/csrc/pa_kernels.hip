@@ -1486,25 +1486,33 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // launch
 // ---------------------------------------------------------------------------
 // Chunked prefill: causal attention of each sequence's last M tokens (a prompt
-// chunk; a decode token is M = 1).  One wave per (query block, kv head,
-// sequence).  A query block is kBlocks column blocks; each fills the 16
-// columns of an MFMA operand holding Q^T with 16 / G queries times the G heads
-// of the kv head.  Every key tile the wave loads into registers, and every
-// value tile it stages in LDS, serves all its column blocks, so the tile
-// traffic per matrix-core operation falls by kBlocks.  Column c of block b is
-// query r = b * 16 / G + c / G of the query block (head c % G) at position
-// T - M + r; key rows after that position get weight zero (its per-lane
-// `live` bound), and the wave streams the tiles up to its last position with
-// the decode kernels' tile math and prefetching.
+// chunk; a decode token is M = 1).  A workgroup of kPrefillWaves waves takes
+// one (query block, kv head, sequence); each wave holds kBlocks column blocks,
+// each filling the 16 columns of an MFMA operand holding Q^T with 16 / G
+// queries times the G heads of the kv head.  Column c of block b of wave w is
+// query r = (w * kBlocks + b) * 16 / G + c / G of the query block (head
+// c % G) at position T - M + r; key rows after that position get weight zero
+// (its per-lane `live` bound).
+//
+// The workgroup walks the keys in 32-key steps up to its last position.  Each
+// step's key and value rows are loaded once, every thread taking a few 16-byte
+// chunks, and staged in LDS, where all the waves' column blocks read them:
+// keys as the A operand of S^T = K . Q^T (row-wise reads, chunks XOR-swizzled
+// per row so that the sixteen rows a read instruction touches fall in distinct
+// banks), values through transposed reads for O^T += V^T . P^T.  Three LDS
+// stages and one barrier per step: the rows of step s + 1 are written while
+// step s is computed, and a stage is rewritten only after every wave has
+// passed the barrier that follows its last reader.
 //
 // Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
 // own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
-// pair after another, so the pair's key and value tiles, read by every one of
+// pair after another, so the pair's key and value rows, read by every one of
 // its query blocks, stay in that XCD's L2.  Pairs are handed out longest
 // sequence first (up to kWave sequences; beyond that in index order), and
-// within a pair the latest query blocks first: the waves with the most keys
-// start early instead of forming a tail.  Which workgroup runs a (pair, query
-// block) does not change its arithmetic, so the results do not depend on it.
+// within a pair the latest query blocks first: the workgroups with the most
+// keys start early instead of forming a tail.  Which workgroup runs a (pair,
+// query block) does not change its arithmetic, so the results do not depend
+// on it.
 // ---------------------------------------------------------------------------
 template <int G>
 struct PrefillShape {
@@ -1519,7 +1527,7 @@ struct PrefillShape {
 // for the length v of rank k -- the largest v with more than k lengths >= v --
 // then the (k - #{lengths > v})-th sequence of length v.
 __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int k, int& len) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x % kWave;
   const int key =
       lane < a.num_seqs ? min(max(a.context_lens[lane], 0), a.max_context_len) : -1;
   uint32_t lo = 0, hi = uint32_t(a.max_context_len) + 1;   // count(lo) > k >= count(hi)
@@ -1615,12 +1623,12 @@ __device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const De
   t.l_run += psum;
 }
 
-// O^T += V^T . P^T over a 32-key step for every column block.  The value
-// tile holds the step's 32 rows in LDS (row r at r * row bytes, 16-byte
-// chunks swizzled per row); a transposed read gives lane (gq, c) four keys of
-// one dimension, 4gq .. 4gq+3 of a half, and the read 16 rows further on the
-// same four keys of the second half: together the A operand chunk matching
-// the weights' order.
+// O^T += V^T . P^T over a 32-key step for every column block.  The step's 32
+// value rows sit in LDS (row r at r * row bytes, 16-byte chunks swizzled per
+// row); a transposed read gives lane (gq, c) four keys of one dimension,
+// 4gq .. 4gq+3 of a half, and the read 16 rows further on the same four keys
+// of the second half: together the A operand chunk matching the weights'
+// order.
 template <int DT, int D, int NB>
 __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const char* vt,
                                              int gq, int c) {
@@ -1634,7 +1642,6 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], con
   uint4 pb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
-  wave_sync_lds();
   const int row = 4 * gq + (c >> 2);
   const char* rbase = vt + row * kRowBytes + ((c & 1) << 3);
   const int sw = MfmaPv<DT, D, 16>::swz(row);
@@ -1649,28 +1656,47 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], con
 #pragma unroll
     for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
   }
-  wave_sync_lds();
+}
+
+// Position of chunk j of key row r in LDS: XOR-swizzled so that the sixteen
+// rows one read instruction takes (same chunk) land in distinct banks.
+template <int DT, int D>
+__device__ __forceinline__ int key_chunk_at(int r, int j) {
+  using GE = Geo<DT, D, 16>;
+  constexpr int kRowsPer256 = 256 / GE::kRowBytes;
+  return r * GE::kRowBytes + ((j ^ ((r / kRowsPer256) & (GE::CPR - 1))) << 4);
 }
 
 template <int DT, int D, int G, bool kTileInBlock>
-__global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, 16>;
-  constexpr int KK = GE::KK, RPI = GE::RPI, VS = GE::VS, CPR = GE::CPR;
+  constexpr int KK = GE::KK, CPR = GE::CPR;
   constexpr int kRowBytes = GE::kRowBytes;
   constexpr int BQ = PrefillShape<G>::kBlockQueries;
   constexpr int NB = PrefillShape<G>::kBlocks;
-  constexpr int QW = PrefillShape<G>::kQueries;
+  constexpr int QW = PrefillShape<G>::kQueries;          // queries per wave
+  constexpr int QG = QW * kPrefillWaves;                  // queries per workgroup
+  constexpr int kThreads = kWave * kPrefillWaves;
+  constexpr int kStepRows = 2 * kTileTokens;              // keys per step
+  constexpr int kLoadRows = kThreads / CPR;               // rows per load instruction
+  constexpr int kLoads = kStepRows / kLoadRows;           // per matrix and step
+  constexpr int kStageBytes = 2 * kStepRows * kRowBytes;  // keys, then values
+  constexpr int kStages = 3;
+  static_assert(kThreads % CPR == 0 && kStepRows % kLoadRows == 0 &&
+                    (kLoadRows % kTileTokens == 0 || kTileTokens % kLoadRows == 0),
+                "load shape");
   using PC = PrefillCols<DT, D>;
-  __shared__ __align__(16) char vtile[2 * kTileTokens * kRowBytes];   // a step's 32 rows
+  __shared__ __align__(16) char lds[kStages * kStageBytes];
 
-  const int nqb = (a.max_query_len - 1) / QW + 1;          // query blocks per pair (>= 1)
+  const int nqb = (a.max_query_len - 1) / QG + 1;          // query blocks per pair (>= 1)
   const int xcd = blockIdx.x % kXcds;
   const int j = blockIdx.x / kXcds;                         // this XCD's j-th workgroup
   const int pair = xcd + kXcds * (j / nqb);                 // pair rank
   if (pair >= a.num_seqs * a.num_kv_heads) return;
   const int rank = pair / a.num_kv_heads;
   const int g = pair - rank * a.num_kv_heads;
-  const int lane = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
   int T, seq;
   if (a.num_seqs <= kWave) {
     seq = seq_of_rank(a, rank, T);
@@ -1680,22 +1706,24 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   }
   const int row_begin = a.query_start[seq];
   const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
-  const int r0 = (nqb - 1 - j % nqb) * QW;                 // latest query blocks first
-  if (r0 >= M) return;
-  const int nq = min(QW, M - r0);
+  const int r0 = (nqb - 1 - j % nqb) * QG;                 // latest query blocks first
+  if (r0 >= M) return;                                      // the whole workgroup
+  const int nq_wg = min(QG, M - r0);
+  const int rw = r0 + wave * QW;                            // this wave's first query
+  const int nq = max(0, min(QW, M - rw));
 
   PC cols[NB];
-  const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
+  const int gq = lane >> 4, c = lane & 15;
   bool col_ok[NB];
   int pos[NB];
   int64_t out_row[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     col_ok[b] = b * BQ + c / G < nq && c < BQ * G;
-    const int qr = r0 + (col_ok[b] ? b * BQ + c / G : 0);   // query row of this column
+    const int qr = rw + (col_ok[b] ? b * BQ + c / G : 0);   // query row of this column
     const int head = g * G + (col_ok[b] ? c % G : 0);
     pos[b] = T - M + qr;                                      // its position
-    out_row[b] = int64_t(row_begin + qr) * a.num_q_heads + head;
+    out_row[b] = int64_t(row_begin + min(qr, M - 1)) * a.num_q_heads + head;
     const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                        out_row[b] * kRowBytes);
 #pragma unroll
@@ -1707,8 +1735,8 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
     cols[b].l_run = 0.0f;
   }
 
-  const int ntiles = (T - M + r0 + nq - 1) / kTileTokens + 1;   // up to the last position
-  const int nsteps = (ntiles + 1) / 2;                          // 32-key steps
+  const int ntiles = (T - M + r0 + nq_wg - 1) / kTileTokens + 1;   // up to the last position
+  const int nsteps = (ntiles + 1) / 2;                             // 32-key steps
   const int lb = a.log2_block;
   const int bmask = (1 << lb) - 1;
   const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
@@ -1717,8 +1745,13 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int nblk = a.num_blocks;
-  const int k_off = c * kRowBytes + gq * 16;
-  const int v_off = rho * kRowBytes + chi * 16;
+  // this thread's share of a step: chunk lchunk of step rows lrow + i * kLoadRows
+  const int lrow = threadIdx.x / CPR, lchunk = threadIdx.x % CPR;
+  // the tile a load instruction of this wave covers, relative to the step's
+  // first tile (the same for all of the wave's lanes)
+  auto load_half = [&](int i) {
+    return (i * kLoadRows + wave * (kWave / CPR)) / kTileTokens;
+  };
 
   // tile k's block (one per lane, 64 tiles per load) when tiles lie in blocks
   int tbl = 0;
@@ -1726,100 +1759,85 @@ __global__ __launch_bounds__(kWave, 2) void prefill_kernel(DecodeArgs a) {
     const int k = min(64 * batch + lane, ntiles - 1);
     tbl = min(max(table[(k * kTileTokens) >> lb], 0), nblk - 1);
   };
-  auto tile_byte = [&](int k) -> int64_t {
-    const int64_t blk = __builtin_amdgcn_readlane(tbl, k & 63);
-    return (blk * blk_rows + head_rows + ((k * kTileTokens) & bmask)) * kRowBytes;
-  };
-  // the buffer spans the tile's rows below T only; a tile past the wave's
-  // last position (the second half of its last step) spans none: its table
-  // lane holds another tile's block, and it must read as zeros
+  // the buffer spans the tile's rows below T only; a tile past the last
+  // position (the second half of the last step) spans none: its table lane
+  // holds another tile's block, and it must read as zeros
   auto rsrc = [&](const char* base, int k) {
+    const int64_t blk = __builtin_amdgcn_readlane(tbl, k & 63);
+    const int64_t byte = (blk * blk_rows + head_rows + ((k * kTileTokens) & bmask)) * kRowBytes;
     const int rows = k < ntiles ? min(kTileTokens, T - k * kTileTokens) : 0;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + tile_byte(k)), 0,
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + byte), 0,
                                              rows * kRowBytes, kBufferDword3);
   };
-  // blocks smaller than a tile: each lane finds its row's block; rows past
-  // T - 1 read row T - 1 (weight zero)
-  auto row_of = [&](int t0, int dt) -> int64_t {
-    const int t = min(t0 + dt, T - 1);
+  // blocks smaller than a tile: each row finds its block; rows past T - 1
+  // read row T - 1 (weight zero)
+  auto row_of = [&](int t) -> int64_t {
+    t = min(t, T - 1);
     const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
     return blk * blk_rows + head_rows + (t & bmask);
   };
-  auto load_keys = [&](int k, KeyRegs<DT, D>& r) {
-    if constexpr (kTileInBlock) {
-      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, k);
+  struct Stage {
+    uint4 k[kLoads], v[kLoads];
+  };
+  auto load_step = [&](int st, Stage& r) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk)
-        r.k[kk] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
-    } else {
-      const uint4* kp = reinterpret_cast<const uint4*>(kbase + row_of(k * kTileTokens, c) * kRowBytes);
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) r.k[kk] = kp[4 * kk + gq];
+    for (int i = 0; i < kLoads; ++i) {
+      const int sr = i * kLoadRows + lrow;                 // row of the step
+      if constexpr (kTileInBlock) {
+        const int k = 2 * st + load_half(i);
+        const int off = (sr % kTileTokens) * kRowBytes + lchunk * 16;
+        r.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsrc(kbase, k), off, 0, 0));
+        r.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsrc(vbase, k), off, 0, 0));
+      } else {
+        const int64_t row = row_of(st * kStepRows + sr);
+        r.k[i] = reinterpret_cast<const uint4*>(kbase + row * kRowBytes)[lchunk];
+        r.v[i] = reinterpret_cast<const uint4*>(vbase + row * kRowBytes)[lchunk];
+      }
     }
   };
-  auto load_values = [&](int k, ValRegs<DT, D>& r) {
-    if constexpr (kTileInBlock) {
-      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, k);
+  auto store_step = [&](const Stage& r, char* st) {
 #pragma unroll
-      for (int s2 = 0; s2 < VS; ++s2)
-        r.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                rv, v_off + s2 * RPI * kRowBytes, 0, 0));
-    } else {
-#pragma unroll
-      for (int s2 = 0; s2 < VS; ++s2)
-        r.v[s2] = reinterpret_cast<const uint4*>(
-            vbase + row_of(k * kTileTokens, s2 * RPI + rho) * kRowBytes)[chi];
-    }
-  };
-  auto stage = [&](const ValRegs<DT, D>& r, char* vt) {
-#pragma unroll
-    for (int s2 = 0; s2 < VS; ++s2) {
-      const int row = s2 * RPI + rho;
-      *reinterpret_cast<uint4*>(vt + row * kRowBytes +
-                                ((chi ^ MfmaPv<DT, D, 16>::swz(row)) << 4)) = r.v[s2];
+    for (int i = 0; i < kLoads; ++i) {
+      const int sr = i * kLoadRows + lrow;
+      *reinterpret_cast<uint4*>(st + key_chunk_at<DT, D>(sr, lchunk)) = r.k[i];
+      *reinterpret_cast<uint4*>(st + kStepRows * kRowBytes + sr * kRowBytes +
+                                ((lchunk ^ MfmaPv<DT, D, 16>::swz(sr)) << 4)) = r.v[i];
     }
   };
 
-  struct StepKeys {
-    KeyRegs<DT, D> h[2];
-  };
   if constexpr (kTileInBlock) load_tbl(0);
-  StepKeys KA, KB;
-  ValRegs<DT, D> V0, V1;
-  load_keys(0, KA.h[0]);
-  load_keys(1, KA.h[1]);
-  load_values(0, V0);
-  load_values(1, V1);
-  if (nsteps > 1) {
-    load_keys(2, KB.h[0]);
-    load_keys(3, KB.h[1]);
-  }
-  auto step = [&](int st, StepKeys& kr) {
-    stage(V0, vtile);
-    stage(V1, vtile + kTileTokens * kRowBytes);
+  Stage R;
+  load_step(0, R);
+  store_step(R, lds);
+  if (nsteps > 1) load_step(1, R);
+  __syncthreads();
+  for (int st = 0; st < nsteps; ++st) {
     if (st + 1 < nsteps) {
-      load_values(2 * st + 2, V0);
-      load_values(2 * st + 3, V1);
+      store_step(R, lds + ((st + 1) % kStages) * kStageBytes);
+      if (st + 2 < nsteps) {
+        if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
+        load_step(st + 2, R);
+      }
     }
+    __syncthreads();
+    const char* kt = lds + (st % kStages) * kStageBytes;
+    KeyRegs<DT, D> kr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kr[h].k[kk] = *reinterpret_cast<const uint4*>(
+            kt + key_chunk_at<DT, D>(h * kTileTokens + c, 4 * kk + gq));
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // keys at positions 32 st .. pos of this column take part
-      const int before = col_ok[b] ? pos[b] - 2 * st * kTileTokens + 1 : 0;
-      prefill_scores32<DT, D>(cols[b], a, kr.h[0], kr.h[1], gq,
-                              min(kTileTokens, max(0, before)),
+      const int before = col_ok[b] ? pos[b] - st * kStepRows + 1 : 0;
+      prefill_scores32<DT, D>(cols[b], a, kr[0], kr[1], gq, min(kTileTokens, max(0, before)),
                               min(kTileTokens, max(0, before - kTileTokens)));
     }
-    if (st + 2 < nsteps) {
-      if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
-      load_keys(2 * st + 4, kr.h[0]);
-      load_keys(2 * st + 5, kr.h[1]);
-    }
-    accumulate32<DT, D, NB>(cols, vtile, gq, c);
-  };
-  for (int st = 0; st < nsteps; st += 2) {
-    step(st, KA);
-    if (st + 1 >= nsteps) break;
-    step(st + 1, KB);
+    accumulate32<DT, D, NB>(cols, kt + kStepRows * kRowBytes, gq, c);
   }
 
 #pragma unroll
@@ -2009,9 +2027,9 @@ hipError_t launch_prefill_g(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<uint32_t>(
         prefill_workgroups(a.num_seqs, a.num_kv_heads, G, a.max_query_len)));
     if (a.log2_block >= 4)
-      launch_timed(prefill_kernel<DT, D, G, true>, grid, dim3(kWave), stream, a);
+      launch_timed(prefill_kernel<DT, D, G, true>, grid, dim3(kWave * kPrefillWaves), stream, a);
     else
-      launch_timed(prefill_kernel<DT, D, G, false>, grid, dim3(kWave), stream, a);
+      launch_timed(prefill_kernel<DT, D, G, false>, grid, dim3(kWave * kPrefillWaves), stream, a);
     return hipGetLastError();
   }
 }

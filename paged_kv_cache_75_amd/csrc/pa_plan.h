@@ -22,10 +22,11 @@ constexpr int32_t kMinSplitTiles = 16;
 // Chunked prefill: 16-column query blocks per wave, and the XCDs whose L2s a
 // launch spreads over (workgroup i runs on XCD i mod kXcds)
 constexpr int32_t kPrefillColumnBlocks = 2;
+constexpr int32_t kPrefillWaves = 4;          // waves per prefill workgroup
 constexpr int32_t kXcds = 8;
 inline int64_t prefill_workgroups(int32_t num_seqs, int32_t num_kv_heads, int32_t group,
                                   int32_t max_query_len) {
-  const int64_t queries = int64_t(16 / group) * kPrefillColumnBlocks;   // per wave
+  const int64_t queries = int64_t(16 / group) * kPrefillColumnBlocks * kPrefillWaves;
   const int64_t blocks = (max_query_len + queries - 1) / queries;
   const int64_t pairs = (int64_t(num_seqs) * num_kv_heads + kXcds - 1) / kXcds * kXcds;
   return blocks * pairs;
