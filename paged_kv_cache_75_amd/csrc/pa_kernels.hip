@@ -1497,9 +1497,8 @@ __global__ __launch_bounds__(kMergeThreads) void lse_reduce_kernel(DecodeArgs a)
 // The workgroup walks the keys in 32-key steps up to its last position.  Each
 // step's key and value rows are loaded once, every thread taking a few 16-byte
 // chunks, and staged in LDS, where all the waves' column blocks read them:
-// keys as the A operand of S^T = K . Q^T (row-wise reads, chunks XOR-swizzled
-// per row so that the sixteen rows a read instruction touches fall in distinct
-// banks), values through transposed reads for O^T += V^T . P^T.  Three LDS
+// keys as the A operand of S^T = K . Q^T (row-wise reads), values through
+// transposed reads for O^T += V^T . P^T (rows padded: PrefillLds).  Three LDS
 // stages and one barrier per step: the rows of step s + 1 are written while
 // step s is computed, and a stage is rewritten only after every wave has
 // passed the barrier that follows its last reader.
@@ -1586,8 +1585,8 @@ struct PrefillCols {
 template <int DT, int D>
 __device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const DecodeArgs& a,
                                                  const KeyRegs<DT, D>& k0,
-                                                 const KeyRegs<DT, D>& k1, int gq, int live0,
-                                                 int live1) {
+                                                 const KeyRegs<DT, D>& k1, int gq, bool mask,
+                                                 int live0, int live1) {
   f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kk = 0; kk < PrefillCols<DT, D>::KK; ++kk) {
@@ -1598,8 +1597,17 @@ __device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const De
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    s[i] = 4 * gq + i < live0 ? s0[i] * a.scale_log2 : -INFINITY;
-    s[4 + i] = 4 * gq + i < live1 ? s1[i] * a.scale_log2 : -INFINITY;
+    s[i] = s0[i] * a.scale_log2;
+    s[4 + i] = s1[i] * a.scale_log2;
+  }
+  // keys after a column's position (a wave-uniform branch: steps on the
+  // diagonal only)
+  if (mask) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (4 * gq + i >= live0) s[i] = -INFINITY;
+      if (4 * gq + i >= live1) s[4 + i] = -INFINITY;
+    }
   }
 #pragma unroll
   for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
@@ -1623,17 +1631,30 @@ __device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const De
   t.l_run += psum;
 }
 
+// LDS rows of a prefill step: key rows padded by 16 bytes and value rows by
+// 32, so that the rows one read instruction touches start in different banks
+// (a key read takes one 16-byte chunk of 16 rows, a transposed value read 32
+// bytes of 8 rows per half-wave) and every read address is a per-lane base
+// plus a constant.
+template <int DT, int D>
+struct PrefillLds {
+  static constexpr int kRowBytes = Geo<DT, D, 16>::kRowBytes;
+  static constexpr int kKeyStride = kRowBytes + 16;
+  static constexpr int kValStride = kRowBytes + 32;
+  static constexpr int kStepRows = 2 * kTileTokens;
+  static constexpr int kValOffset = kStepRows * kKeyStride;
+  static constexpr int kStageBytes = kValOffset + kStepRows * kValStride;
+};
+
 // O^T += V^T . P^T over a 32-key step for every column block.  The step's 32
-// value rows sit in LDS (row r at r * row bytes, 16-byte chunks swizzled per
-// row); a transposed read gives lane (gq, c) four keys of one dimension,
-// 4gq .. 4gq+3 of a half, and the read 16 rows further on the same four keys
-// of the second half: together the A operand chunk matching the weights'
-// order.
+// value rows sit in LDS at the padded stride; a transposed read gives lane
+// (gq, c) four keys of one dimension, 4gq .. 4gq+3 of a half, and the read 16
+// rows further on the same four keys of the second half: together the A
+// operand chunk matching the weights' order.
 template <int DT, int D, int NB>
 __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const char* vt,
                                              int gq, int c) {
-  using GE = Geo<DT, D, 16>;
-  constexpr int kRowBytes = GE::kRowBytes;
+  constexpr int kValStride = PrefillLds<DT, D>::kValStride;
   // two four-element halves as one eight-element operand chunk
   auto join = [](v4i16 lo, v4i16 hi) {
     const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
@@ -1642,29 +1663,19 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], con
   uint4 pb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
-  const int row = 4 * gq + (c >> 2);
-  const char* rbase = vt + row * kRowBytes + ((c & 1) << 3);
-  const int sw = MfmaPv<DT, D, 16>::swz(row);
+  // lane (gq, c): row 4gq + c/4, dimensions 16n + 4(c%4) .. +3
+  const char* rbase = vt + (4 * gq + (c >> 2)) * kValStride + ((c & 1) << 3) +
+                      (((c & 3) >> 1) << 4);
 #pragma unroll
   for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) {
-    const int chunk = 2 * n + ((c & 3) >> 1);
-    const char* at = rbase + ((chunk ^ sw) << 4);
+    const char* at = rbase + 32 * n;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
     const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kRowBytes));
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kValStride));
     const uint4 av = join(lo, hi);
 #pragma unroll
     for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
   }
-}
-
-// Position of chunk j of key row r in LDS: XOR-swizzled so that the sixteen
-// rows one read instruction takes (same chunk) land in distinct banks.
-template <int DT, int D>
-__device__ __forceinline__ int key_chunk_at(int r, int j) {
-  using GE = Geo<DT, D, 16>;
-  constexpr int kRowsPer256 = 256 / GE::kRowBytes;
-  return r * GE::kRowBytes + ((j ^ ((r / kRowsPer256) & (GE::CPR - 1))) << 4);
 }
 
 template <int DT, int D, int G, bool kTileInBlock>
@@ -1680,7 +1691,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   constexpr int kStepRows = 2 * kTileTokens;              // keys per step
   constexpr int kLoadRows = kThreads / CPR;               // rows per load instruction
   constexpr int kLoads = kStepRows / kLoadRows;           // per matrix and step
-  constexpr int kStageBytes = 2 * kStepRows * kRowBytes;  // keys, then values
+  using LS = PrefillLds<DT, D>;
+  constexpr int kStageBytes = LS::kStageBytes;            // keys, then values
   constexpr int kStages = 3;
   static_assert(kThreads % CPR == 0 && kStepRows % kLoadRows == 0 &&
                     (kLoadRows % kTileTokens == 0 || kTileTokens % kLoadRows == 0),
@@ -1735,6 +1747,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     cols[b].l_run = 0.0f;
   }
 
+  // the wave's first position; a wave with no queries computes columns it
+  // never stores, so any bound serves it
+  const int first_pos = T - M + rw;
   const int ntiles = (T - M + r0 + nq_wg - 1) / kTileTokens + 1;   // up to the last position
   const int nsteps = (ntiles + 1) / 2;                             // 32-key steps
   const int lb = a.log2_block;
@@ -1801,9 +1816,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int sr = i * kLoadRows + lrow;
-      *reinterpret_cast<uint4*>(st + key_chunk_at<DT, D>(sr, lchunk)) = r.k[i];
-      *reinterpret_cast<uint4*>(st + kStepRows * kRowBytes + sr * kRowBytes +
-                                ((lchunk ^ MfmaPv<DT, D, 16>::swz(sr)) << 4)) = r.v[i];
+      *reinterpret_cast<uint4*>(st + sr * LS::kKeyStride + lchunk * 16) = r.k[i];
+      *reinterpret_cast<uint4*>(st + LS::kValOffset + sr * LS::kValStride + lchunk * 16) =
+          r.v[i];
     }
   };
 
@@ -1823,21 +1838,27 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     }
     __syncthreads();
     const char* kt = lds + (st % kStages) * kStageBytes;
+    // lane (gq, c): key row c of each half, chunks 4kk + gq
+    const char* kb = kt + c * LS::kKeyStride + gq * 16;
     KeyRegs<DT, D> kr[2];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kr[h].k[kk] = *reinterpret_cast<const uint4*>(
-            kt + key_chunk_at<DT, D>(h * kTileTokens + c, 4 * kk + gq));
+        kr[h].k[kk] = *reinterpret_cast<const uint4*>(kb + h * kTileTokens * LS::kKeyStride +
+                                                      64 * kk);
+    // masking is needed unless every key of the step precedes every
+    // column's position
+    const bool mask = (st + 1) * kStepRows - 1 > first_pos;
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // keys at positions 32 st .. pos of this column take part
       const int before = col_ok[b] ? pos[b] - st * kStepRows + 1 : 0;
-      prefill_scores32<DT, D>(cols[b], a, kr[0], kr[1], gq, min(kTileTokens, max(0, before)),
+      prefill_scores32<DT, D>(cols[b], a, kr[0], kr[1], gq, mask,
+                              min(kTileTokens, max(0, before)),
                               min(kTileTokens, max(0, before - kTileTokens)));
     }
-    accumulate32<DT, D, NB>(cols, kt + kStepRows * kRowBytes, gq, c);
+    accumulate32<DT, D, NB>(cols, kt + LS::kValOffset, gq, c);
   }
 
 #pragma unroll
