@@ -1631,15 +1631,18 @@ __device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const De
   t.l_run += psum;
 }
 
-// LDS rows of a prefill step: key rows padded by 16 bytes and value rows by
-// 32, so that the rows one read instruction touches start in different banks
-// (a key read takes one 16-byte chunk of 16 rows, a transposed value read 32
-// bytes of 8 rows per half-wave) and every read address is a per-lane base
-// plus a constant.
+// LDS rows of a prefill step, key and value rows both padded by 32 bytes.
+// The LDS serves 32 lanes per pass from 128 four-byte banks; with a row
+// stride of 72 (or 40) words, 16 consecutive rows start on 16 distinct
+// multiples of 8 banks, so a key read (16 bytes of 16 rows for 32 lanes) and
+// a transposed value read (32 bytes of 8 rows for 32 lanes) find no conflict,
+// and every read address is a per-lane base plus a constant.  The staging
+// writes take rows r, r + 8 (r, r + 4, r + 8, r + 12 for 128-byte rows) in
+// one pass, whose 256-byte spans are disjoint modulo 512 bytes.
 template <int DT, int D>
 struct PrefillLds {
   static constexpr int kRowBytes = Geo<DT, D, 16>::kRowBytes;
-  static constexpr int kKeyStride = kRowBytes + 16;
+  static constexpr int kKeyStride = kRowBytes + 32;
   static constexpr int kValStride = kRowBytes + 32;
   static constexpr int kStepRows = 2 * kTileTokens;
   static constexpr int kValOffset = kStepRows * kKeyStride;
@@ -1760,8 +1763,11 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
   const int nblk = a.num_blocks;
-  // this thread's share of a step: chunk lchunk of step rows lrow + i * kLoadRows
-  const int lrow = threadIdx.x / CPR, lchunk = threadIdx.x % CPR;
+  // this thread's share of a step: chunk lchunk of step rows lrow + i * kLoadRows,
+  // the rows of one 32-lane pass spread as the LDS layout wants
+  constexpr int kPassRows = 32 / CPR;
+  const int q = threadIdx.x / CPR, lchunk = threadIdx.x % CPR;
+  const int lrow = (q & ~15) + (q & 15) / kPassRows + (16 / kPassRows) * (q % kPassRows);
   // the tile a load instruction of this wave covers, relative to the step's
   // first tile (the same for all of the wave's lanes)
   auto load_half = [&](int i) {
