@@ -1583,16 +1583,23 @@ struct PrefillCols {
 // 16x16x32 product O^T += V^T . P^T (the contraction over keys may take them
 // in any order, as long as V^T's chunks follow the same order).
 template <int DT, int D>
-__device__ __forceinline__ void prefill_scores32(PrefillCols<DT, D>& t, const DecodeArgs& a,
-                                                 const KeyRegs<DT, D>& k0,
-                                                 const KeyRegs<DT, D>& k1, int gq, bool mask,
-                                                 int live0, int live1) {
-  f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+__device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
+                                             const KeyRegs<DT, D>& k0, const KeyRegs<DT, D>& k1,
+                                             f32x4& s0, f32x4& s1) {
+  s0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  s1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
   for (int kk = 0; kk < PrefillCols<DT, D>::KK; ++kk) {
     s0 = mfma_chunk<DT>(k0.k[kk], t.qb[kk], s0);
     s1 = mfma_chunk<DT>(k1.k[kk], t.qb[kk], s1);
   }
+}
+
+// The step's weights from its raw scores s0, s1 (S^T = K . Q^T per half).
+template <int DT, int D>
+__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D>& t, const DecodeArgs& a,
+                                                  f32x4 s0, f32x4 s1, int gq, bool mask,
+                                                  int live0, int live1) {
   float s[8];
   float mx = -INFINITY;
 #pragma unroll
@@ -1828,21 +1835,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     }
   };
 
-  if constexpr (kTileInBlock) load_tbl(0);
   Stage R;
-  load_step(0, R);
-  store_step(R, lds);
-  if (nsteps > 1) load_step(1, R);
-  __syncthreads();
-  for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps) {
-      store_step(R, lds + ((st + 1) % kStages) * kStageBytes);
-      if (st + 2 < nsteps) {
-        if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
-        load_step(st + 2, R);
-      }
-    }
-    __syncthreads();
+  // S^T of a step for every column block (keys from the step's LDS stage)
+  using Scores = f32x4[NB][2];
+  auto qk = [&](int st, Scores& sc) {
     const char* kt = lds + (st % kStages) * kStageBytes;
     // lane (gq, c): key row c of each half, chunks 4kk + gq
     const char* kb = kt + c * LS::kKeyStride + gq * 16;
@@ -1853,6 +1849,23 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       for (int kk = 0; kk < KK; ++kk)
         kr[h].k[kk] = *reinterpret_cast<const uint4*>(kb + h * kTileTokens * LS::kKeyStride +
                                                       64 * kk);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) prefill_qk32<DT, D>(cols[b], kr[0], kr[1], sc[b][0], sc[b][1]);
+  };
+  // Step st: stage the rows of step st + 1 and fetch those of st + 2; after
+  // the barrier, step st + 1's rows are complete too, so its scores go to the
+  // matrix cores before step st's softmax and P.V (`cur` holds step st's
+  // scores, `next` receives step st + 1's).
+  auto step = [&](int st, Scores& cur, Scores& next) {
+    if (st + 1 < nsteps) {
+      store_step(R, lds + ((st + 1) % kStages) * kStageBytes);
+      if (st + 2 < nsteps) {
+        if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
+        load_step(st + 2, R);
+      }
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) qk(st + 1, next);
     // masking is needed unless every key of the step precedes every
     // column's position
     const bool mask = (st + 1) * kStepRows - 1 > first_pos;
@@ -1860,11 +1873,24 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     for (int b = 0; b < NB; ++b) {
       // keys at positions 32 st .. pos of this column take part
       const int before = col_ok[b] ? pos[b] - st * kStepRows + 1 : 0;
-      prefill_scores32<DT, D>(cols[b], a, kr[0], kr[1], gq, mask,
-                              min(kTileTokens, max(0, before)),
-                              min(kTileTokens, max(0, before - kTileTokens)));
+      prefill_softmax32<DT, D>(cols[b], a, cur[b][0], cur[b][1], gq, mask,
+                               min(kTileTokens, max(0, before)),
+                               min(kTileTokens, max(0, before - kTileTokens)));
     }
-    accumulate32<DT, D, NB>(cols, kt + LS::kValOffset, gq, c);
+    accumulate32<DT, D, NB>(cols, lds + (st % kStages) * kStageBytes + LS::kValOffset, gq, c);
+  };
+
+  if constexpr (kTileInBlock) load_tbl(0);
+  load_step(0, R);
+  store_step(R, lds);
+  if (nsteps > 1) load_step(1, R);
+  __syncthreads();
+  Scores SA, SB;
+  qk(0, SA);
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, SA, SB);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, SB, SA);
   }
 
 #pragma unroll
