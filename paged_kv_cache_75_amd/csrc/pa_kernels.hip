@@ -1595,47 +1595,62 @@ __device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
   }
 }
 
-// The step's weights from its raw scores s0, s1 (S^T = K . Q^T per half).
-template <int DT, int D>
-__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D>& t, const DecodeArgs& a,
-                                                  f32x4 s0, f32x4 s1, int gq, bool mask,
-                                                  int live0, int live1) {
-  float s[8];
-  float mx = -INFINITY;
+// The step's weights for every column block from its raw scores (S^T =
+// K . Q^T per half): scaled, masked on diagonal steps, column maxima, then
+// one wave-uniform test for a reference move in any block, then the weights.
+template <int DT, int D, int NB>
+__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB],
+                                                  const DecodeArgs& a, const f32x4 (&sc)[NB][2],
+                                                  int gq, bool mask, const int (&live)[NB][2]) {
+  float s[NB][8], mx[NB];
+  bool move = false;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    s[i] = s0[i] * a.scale_log2;
-    s[4 + i] = s1[i] * a.scale_log2;
-  }
-  // keys after a column's position (a wave-uniform branch: steps on the
-  // diagonal only)
-  if (mask) {
+  for (int b = 0; b < NB; ++b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      if (4 * gq + i >= live0) s[i] = -INFINITY;
-      if (4 * gq + i >= live1) s[4 + i] = -INFINITY;
+      s[b][i] = sc[b][0][i] * a.scale_log2;
+      s[b][4 + i] = sc[b][1][i] * a.scale_log2;
+    }
+    // keys after a column's position (a wave-uniform branch: steps on the
+    // diagonal only)
+    if (mask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * gq + i >= live[b][0]) s[b][i] = -INFINITY;
+        if (4 * gq + i >= live[b][1]) s[b][4 + i] = -INFINITY;
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, s[b][i]);
+    mx[b] = column_max(m);
+    move |= mx[b] > cols[b].m_run + kRefSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      PrefillCols<DT, D>& t = cols[b];
+      const float m_new = fmaxf(t.m_run, mx[b]);
+      // a column with nothing so far (m_new = -inf) has nothing to rescale
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
+      t.l_run *= alpha;
+      t.m_run = m_new;
     }
   }
 #pragma unroll
-  for (int i = 0; i < 8; ++i) mx = fmaxf(mx, s[i]);
-  mx = column_max(mx);
-  if (__builtin_amdgcn_ballot_w64(mx > t.m_run + kRefSlack) != 0) {
-    const float m_new = fmaxf(t.m_run, mx);
-    // a column with nothing so far (m_new = -inf) has nothing to rescale
-    const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
+  for (int b = 0; b < NB; ++b) {
+    PrefillCols<DT, D>& t = cols[b];
+    const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
+    float psum = 0.0f;
 #pragma unroll
-    for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
-    t.l_run *= alpha;
-    t.m_run = m_new;
+    for (int i = 0; i < 8; ++i) {
+      t.p[i] = __builtin_amdgcn_exp2f(s[b][i] - m_use);
+      psum += t.p[i];
+    }
+    t.l_run += psum;
   }
-  const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
-  float psum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    t.p[i] = __builtin_amdgcn_exp2f(s[i] - m_use);
-    psum += t.p[i];
-  }
-  t.l_run += psum;
 }
 
 // LDS rows of a prefill step, key and value rows both padded by 32 bytes.
@@ -1869,14 +1884,15 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     // masking is needed unless every key of the step precedes every
     // column's position
     const bool mask = (st + 1) * kStepRows - 1 > first_pos;
+    int live[NB][2];
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       // keys at positions 32 st .. pos of this column take part
       const int before = col_ok[b] ? pos[b] - st * kStepRows + 1 : 0;
-      prefill_softmax32<DT, D>(cols[b], a, cur[b][0], cur[b][1], gq, mask,
-                               min(kTileTokens, max(0, before)),
-                               min(kTileTokens, max(0, before - kTileTokens)));
+      live[b][0] = min(kTileTokens, max(0, before));
+      live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
+    prefill_softmax32<DT, D, NB>(cols, a, cur, gq, mask, live);
     accumulate32<DT, D, NB>(cols, lds + (st % kStages) * kStageBytes + LS::kValOffset, gq, c);
   };
 
