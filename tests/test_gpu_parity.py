@@ -426,7 +426,7 @@ def test_sliding_window_covering_everything_is_pa_decode():
 # ---------------------------------------------------------------------------
 # pa_prefill: causal attention of each sequence's last M_i tokens
 # ---------------------------------------------------------------------------
-def _prefill_case(w, mq, seed, label, sample_rows=None):
+def _prefill_case(w, mq, seed, label, sample_rows=None, scale=None):
     import torch
     from workloads.generate import round_to_dtype
     from paged_kv_cache_75_amd import pa_prefill, pa_write_kv
@@ -439,14 +439,15 @@ def _prefill_case(w, mq, seed, label, sample_rows=None):
     pa_write_kv(dw.new_k, dw.new_v, dw.slot_mapping, dw.k_pool, dw.v_pool)
     from gpu_util import to_device
     out = pa_prefill(to_device(q, w.dtype, DEV), dw.k_pool, dw.v_pool, dw.block_tables,
-                     dw.context_lens, to_device(qs, None, DEV), w.scale,
+                     dw.context_lens, to_device(qs, None, DEV), w.scale if scale is None else scale,
                      max_context_len=w.max_context_len, max_query_len=int(max(mq)))
     _sync()
     k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size,
                         inplace=sample_rows is not None)
     got = to_f64(out)
     if sample_rows is None:
-        want = ref.prefill(q, k, v, w.block_tables, w.context_lens, mq, w.scale, w.dtype)
+        want = ref.prefill(q, k, v, w.block_tables, w.context_lens, mq,
+                           w.scale if scale is None else scale, w.dtype)
         compare(got, want, w.dtype, label=label)
     else:
         # sequences picked whole: the oracle runs on those only
@@ -470,6 +471,18 @@ def test_prefill_mixed_batch(dtype, block_size, group, head_dim):
     w = workloads.random_paged("prefill", dtype, hkv * group, hkv, head_dim, block_size, lens,
                                seed=1800 + group + block_size, spare_frac=0.1)
     _prefill_case(w, mq, 1900 + group, f"{dtype} B={block_size} G={group} D={head_dim}")
+
+
+@pytest.mark.parametrize("scale", [-0.11, 0.0, 0.5])
+def test_prefill_scale_sign(scale):
+    """Any finite scale: a negative one (the softmax then favours the
+    smallest scores), zero (uniform weights over the attended keys) and a
+    large positive one."""
+    lens = [1, 40, 100, 33, 257]
+    mq = [1, 40, 17, 33, 64]
+    w = workloads.random_paged("prefill-scale", "bf16", 8, 2, 128, 16, lens, seed=2400,
+                               spare_frac=0.1)
+    _prefill_case(w, mq, 2401, f"scale {scale}", scale=scale)
 
 
 @pytest.mark.parametrize("num_seqs", [64, 65])
