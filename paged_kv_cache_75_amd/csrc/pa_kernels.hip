@@ -383,6 +383,7 @@ typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef _Float16 v4f16 __attribute__((ext_vector_type(4)));
 typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+typedef __attribute__((address_space(3))) char lds_char;
 
 template <int DT> __device__ inline f32x4 mfma_pv(v4i16 a, v4i16 b, f32x4 acc);
 template <> __device__ inline f32x4 mfma_pv<PA_BF16>(v4i16 a, v4i16 b, f32x4 acc) {
@@ -1672,13 +1673,13 @@ struct PrefillLds {
 };
 
 // O^T += V^T . P^T over a 32-key step for every column block.  The step's 32
-// value rows sit in LDS at the padded stride; a transposed read gives lane
-// (gq, c) four keys of one dimension, 4gq .. 4gq+3 of a half, and the read 16
-// rows further on the same four keys of the second half: together the A
-// operand chunk matching the weights' order.
+// value rows sit in LDS at the padded stride; `rbase` points at lane (gq,
+// c)'s first read: row 4gq + c/4 of the first half, dimensions 4(c%4) .. +3.
+// A transposed read gives the lane four keys of one dimension, 4gq .. 4gq+3
+// of a half, and the read 16 rows further on the same four keys of the
+// second half: together the A operand chunk matching the weights' order.
 template <int DT, int D, int NB>
-__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const char* vt,
-                                             int gq, int c) {
+__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], lds_char* rbase) {
   constexpr int kValStride = PrefillLds<DT, D>::kValStride;
   // two four-element halves as one eight-element operand chunk
   auto join = [](v4i16 lo, v4i16 hi) {
@@ -1688,12 +1689,9 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], con
   uint4 pb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
-  // lane (gq, c): row 4gq + c/4, dimensions 16n + 4(c%4) .. +3
-  const char* rbase = vt + (4 * gq + (c >> 2)) * kValStride + ((c & 1) << 3) +
-                      (((c & 3) >> 1) << 4);
 #pragma unroll
   for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) {
-    const char* at = rbase + 32 * n;
+    lds_char* at = rbase + 32 * n;
     const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
     const v4i16 hi =
         __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kValStride));
@@ -1851,10 +1849,19 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   };
 
   Stage R;
+  // lane (gq, c) reads value row 4gq + c/4, dimensions 16n + 4(c%4) .. +3 of
+  // each step (a local-memory pointer: stage and constants fold into the
+  // read instructions' offsets)
+  lds_char* const lds_v = (lds_char*)lds + LS::kValOffset +
+                          (4 * gq + (c >> 2)) * LS::kValStride + ((c & 1) << 3) +
+                          (((c & 3) >> 1) << 4);
+  // byte offset of step st's LDS stage, unsigned so that the compiler can
+  // fold each read's constant part into the instruction's offset field
+  auto stage_of = [](int st) -> uint32_t { return uint32_t(st) % kStages * kStageBytes; };
   // S^T of a step for every column block (keys from the step's LDS stage)
   using Scores = f32x4[NB][2];
   auto qk = [&](int st, Scores& sc) {
-    const char* kt = lds + (st % kStages) * kStageBytes;
+    const char* kt = lds + stage_of(st);
     // lane (gq, c): key row c of each half, chunks 4kk + gq
     const char* kb = kt + c * LS::kKeyStride + gq * 16;
     KeyRegs<DT, D> kr[2];
@@ -1873,7 +1880,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   // scores, `next` receives step st + 1's).
   auto step = [&](int st, Scores& cur, Scores& next) {
     if (st + 1 < nsteps) {
-      store_step(R, lds + ((st + 1) % kStages) * kStageBytes);
+      store_step(R, lds + stage_of(st + 1));
       if (st + 2 < nsteps) {
         if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
         load_step(st + 2, R);
@@ -1893,7 +1900,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
     prefill_softmax32<DT, D, NB>(cols, a, cur, gq, mask, live);
-    accumulate32<DT, D, NB>(cols, lds + (st % kStages) * kStageBytes + LS::kValOffset, gq, c);
+    accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
   };
 
   if constexpr (kTileInBlock) load_tbl(0);
