@@ -1,0 +1,520 @@
+// Chunked prefill attention for gfx950 (pa_prefill): causal attention of
+// each sequence's newest M tokens through its block table, on the matrix
+// cores, with K/V rows shared by the waves of a workgroup through LDS.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "pa_device.h"
+#include "pa_kernels.h"
+#include "pa_launch.h"
+
+namespace pa {
+
+namespace {
+
+// Chunked prefill: causal attention of each sequence's last M tokens (a prompt
+// chunk; a decode token is M = 1).  A workgroup of kPrefillWaves waves takes
+// one (query block, kv head, sequence); each wave holds kBlocks column blocks,
+// each filling the 16 columns of an MFMA operand holding Q^T with 16 / G
+// queries times the G heads of the kv head.  Column c of block b of wave w is
+// query r = (w * kBlocks + b) * 16 / G + c / G of the query block (head
+// c % G) at position T - M + r; key rows after that position get weight zero
+// (its per-lane `live` bound).
+//
+// The workgroup walks the keys in 32-key steps up to its last position.  Each
+// step's key and value rows are loaded once, every thread taking a few 16-byte
+// chunks, and staged in LDS, where all the waves' column blocks read them:
+// keys as the A operand of S^T = K . Q^T (row-wise reads), values through
+// transposed reads for O^T += V^T . P^T (rows padded: PrefillLds).  Three LDS
+// stages and one barrier per step: the rows of step s + 1 are written while
+// step s is computed, and a stage is rewritten only after every wave has
+// passed the barrier that follows its last reader.
+//
+// Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
+// own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
+// pair after another, so the pair's key and value rows, read by every one of
+// its query blocks, stay in that XCD's L2.  Pairs are handed out longest
+// sequence first (up to kWave sequences; beyond that in index order), and
+// within a pair the latest query blocks first: the workgroups with the most
+// keys start early instead of forming a tail.  Which workgroup runs a (pair,
+// query block) does not change its arithmetic, so the results do not depend
+// on it.
+// ---------------------------------------------------------------------------
+template <int G>
+struct PrefillShape {
+  static constexpr int kBlockQueries = 16 / G;          // queries per column block
+  static constexpr int kBlocks = kPrefillColumnBlocks;  // column blocks per wave
+  static constexpr int kQueries = kBlockQueries * kBlocks;
+};
+
+// The sequence of rank k when sequences are ordered by clamped length,
+// longest first, equal lengths by index (num_seqs <= kWave: lane s holds
+// sequence s's length; every workgroup derives the same order).  Binary search
+// for the length v of rank k -- the largest v with more than k lengths >= v --
+// then the (k - #{lengths > v})-th sequence of length v.
+__device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int k, int& len) {
+  const int lane = threadIdx.x % kWave;
+  const int key =
+      lane < a.num_seqs ? min(max(a.context_lens[lane], 0), a.max_context_len) : -1;
+  uint32_t lo = 0, hi = uint32_t(a.max_context_len) + 1;   // count(lo) > k >= count(hi)
+  while (hi - lo > 1) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    if (__popcll(__builtin_amdgcn_ballot_w64(key >= int(mid))) > k) lo = mid;
+    else hi = mid;
+  }
+  const int v = int(lo);
+  const int m = k - __popcll(__builtin_amdgcn_ballot_w64(key > v));
+  const uint64_t eq = __builtin_amdgcn_ballot_w64(key == v);
+  const int below = __builtin_amdgcn_mbcnt_hi(uint32_t(eq >> 32),
+                                              __builtin_amdgcn_mbcnt_lo(uint32_t(eq), 0));
+  const int s = __ffsll(static_cast<long long>(
+                    __builtin_amdgcn_ballot_w64(key == v && below == m))) - 1;
+  len = v;
+  return s;
+}
+
+// The maximum over the four lanes of each column (lanes c, c + 16, c + 32,
+// c + 48): row swaps on the vector ALU rather than permutes through LDS.
+__device__ __forceinline__ float column_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+
+// Softmax reference of the prefill: a column keeps its reference m until a
+// step's maximum exceeds it by more than kRefSlack (log2 units); only then are
+// the wave's sums and outputs rescaled (a wave-uniform branch).  The result is
+// the same softmax: every weight exp2(s - m) stays at most 2^kRefSlack, well
+// inside float32 and bfloat16 range, and the relative precision of the
+// weights does not depend on their scale.
+constexpr float kRefSlack = 8.0f;
+
+// One 16-column block of a prefill wave: Q^T operand, O^T accumulators, the
+// running reference and sum, and the step's weights.
+template <int DT, int D>
+struct PrefillCols {
+  static constexpr int KK = D / 32;            // 32-element chunks of a query row
+  static constexpr int NT = D / 16;            // 16-row tiles of O^T
+  uint4 qb[KK];
+  f32x4 o[NT];
+  float m_run, l_run;
+  float p[8];                                  // keys 4gq + i of each 16-key half
+};
+
+// A step is 32 keys: two 16-key tiles (halves).  S^T = K . Q^T per half gives
+// lane (gq, c) the scores of keys 4gq .. 4gq+3 of each half for column c;
+// those eight weights are, in that order, the lane's B operand of the
+// 16x16x32 product O^T += V^T . P^T (the contraction over keys may take them
+// in any order, as long as V^T's chunks follow the same order).
+template <int DT, int D>
+__device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
+                                             const KeyRegs<DT, D>& k0, const KeyRegs<DT, D>& k1,
+                                             f32x4& s0, f32x4& s1) {
+  s0 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  s1 = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int kk = 0; kk < PrefillCols<DT, D>::KK; ++kk) {
+    s0 = mfma_chunk<DT>(k0.k[kk], t.qb[kk], s0);
+    s1 = mfma_chunk<DT>(k1.k[kk], t.qb[kk], s1);
+  }
+}
+
+// The step's weights for every column block from its raw scores (S^T =
+// K . Q^T per half): scaled, masked on diagonal steps, column maxima, then
+// one wave-uniform test for a reference move in any block, then the weights.
+template <int DT, int D, int NB>
+__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB],
+                                                  const DecodeArgs& a, const f32x4 (&sc)[NB][2],
+                                                  int gq, bool mask, const int (&live)[NB][2]) {
+  float s[NB][8], mx[NB];
+  bool move = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      s[b][i] = sc[b][0][i] * a.scale_log2;
+      s[b][4 + i] = sc[b][1][i] * a.scale_log2;
+    }
+    // keys after a column's position (a wave-uniform branch: steps on the
+    // diagonal only)
+    if (mask) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (4 * gq + i >= live[b][0]) s[b][i] = -INFINITY;
+        if (4 * gq + i >= live[b][1]) s[b][4 + i] = -INFINITY;
+      }
+    }
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, s[b][i]);
+    mx[b] = column_max(m);
+    move |= mx[b] > cols[b].m_run + kRefSlack;
+  }
+  if (__builtin_amdgcn_ballot_w64(move) != 0) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      PrefillCols<DT, D>& t = cols[b];
+      const float m_new = fmaxf(t.m_run, mx[b]);
+      // a column with nothing so far (m_new = -inf) has nothing to rescale
+      const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
+#pragma unroll
+      for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
+      t.l_run *= alpha;
+      t.m_run = m_new;
+    }
+  }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    PrefillCols<DT, D>& t = cols[b];
+    const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
+    float psum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      t.p[i] = __builtin_amdgcn_exp2f(s[b][i] - m_use);
+      psum += t.p[i];
+    }
+    t.l_run += psum;
+  }
+}
+
+// LDS rows of a prefill step, key and value rows both padded by 32 bytes.
+// The LDS serves 32 lanes per pass from 128 four-byte banks; with a row
+// stride of 72 (or 40) words, 16 consecutive rows start on 16 distinct
+// multiples of 8 banks, so a key read (16 bytes of 16 rows for 32 lanes) and
+// a transposed value read (32 bytes of 8 rows for 32 lanes) find no conflict,
+// and every read address is a per-lane base plus a constant.  The staging
+// writes take rows r, r + 8 (r, r + 4, r + 8, r + 12 for 128-byte rows) in
+// one pass, whose 256-byte spans are disjoint modulo 512 bytes.
+template <int DT, int D>
+struct PrefillLds {
+  static constexpr int kRowBytes = Geo<DT, D, 16>::kRowBytes;
+  static constexpr int kKeyStride = kRowBytes + 32;
+  static constexpr int kValStride = kRowBytes + 32;
+  static constexpr int kStepRows = 2 * kTileTokens;
+  static constexpr int kValOffset = kStepRows * kKeyStride;
+  static constexpr int kStageBytes = kValOffset + kStepRows * kValStride;
+};
+
+// O^T += V^T . P^T over a 32-key step for every column block.  The step's 32
+// value rows sit in LDS at the padded stride; `rbase` points at lane (gq,
+// c)'s first read: row 4gq + c/4 of the first half, dimensions 4(c%4) .. +3.
+// A transposed read gives the lane four keys of one dimension, 4gq .. 4gq+3
+// of a half, and the read 16 rows further on the same four keys of the
+// second half: together the A operand chunk matching the weights' order.
+template <int DT, int D, int NB>
+__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], lds_char* rbase) {
+  constexpr int kValStride = PrefillLds<DT, D>::kValStride;
+  // two four-element halves as one eight-element operand chunk
+  auto join = [](v4i16 lo, v4i16 hi) {
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    return make_uint4(l.x, l.y, h.x, h.y);
+  };
+  uint4 pb[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
+#pragma unroll
+  for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) {
+    lds_char* at = rbase + 32 * n;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kValStride));
+    const uint4 av = join(lo, hi);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
+  }
+}
+
+template <int DT, int D, int G, bool kTileInBlock>
+__global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(DecodeArgs a) {
+  using GE = Geo<DT, D, 16>;
+  constexpr int KK = GE::KK, CPR = GE::CPR;
+  constexpr int kRowBytes = GE::kRowBytes;
+  constexpr int BQ = PrefillShape<G>::kBlockQueries;
+  constexpr int NB = PrefillShape<G>::kBlocks;
+  constexpr int QW = PrefillShape<G>::kQueries;          // queries per wave
+  constexpr int QG = QW * kPrefillWaves;                  // queries per workgroup
+  constexpr int kThreads = kWave * kPrefillWaves;
+  constexpr int kStepRows = 2 * kTileTokens;              // keys per step
+  constexpr int kLoadRows = kThreads / CPR;               // rows per load instruction
+  constexpr int kLoads = kStepRows / kLoadRows;           // per matrix and step
+  using LS = PrefillLds<DT, D>;
+  constexpr int kStageBytes = LS::kStageBytes;            // keys, then values
+  constexpr int kStages = 3;
+  static_assert(kThreads % CPR == 0 && kStepRows % kLoadRows == 0 &&
+                    (kLoadRows % kTileTokens == 0 || kTileTokens % kLoadRows == 0),
+                "load shape");
+  using PC = PrefillCols<DT, D>;
+  __shared__ __align__(16) char lds[kStages * kStageBytes];
+
+  const int nqb = (a.max_query_len - 1) / QG + 1;          // query blocks per pair (>= 1)
+  const int xcd = blockIdx.x % kXcds;
+  const int j = blockIdx.x / kXcds;                         // this XCD's j-th workgroup
+  const int pair = xcd + kXcds * (j / nqb);                 // pair rank
+  if (pair >= a.num_seqs * a.num_kv_heads) return;
+  const int rank = pair / a.num_kv_heads;
+  const int g = pair - rank * a.num_kv_heads;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int lane = threadIdx.x % kWave;
+  int T, seq;
+  if (a.num_seqs <= kWave) {
+    seq = seq_of_rank(a, rank, T);
+  } else {
+    seq = rank;
+    T = min(max(a.context_lens[seq], 0), a.max_context_len);
+  }
+  const int row_begin = a.query_start[seq];
+  const int M = min(max(a.query_start[seq + 1] - row_begin, 0), T);
+  const int r0 = (nqb - 1 - j % nqb) * QG;                 // latest query blocks first
+  if (r0 >= M) return;                                      // the whole workgroup
+  const int nq_wg = min(QG, M - r0);
+  const int rw = r0 + wave * QW;                            // this wave's first query
+  const int nq = max(0, min(QW, M - rw));
+
+  PC cols[NB];
+  const int gq = lane >> 4, c = lane & 15;
+  bool col_ok[NB];
+  int pos[NB];
+  int64_t out_row[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    col_ok[b] = b * BQ + c / G < nq && c < BQ * G;
+    const int qr = rw + (col_ok[b] ? b * BQ + c / G : 0);   // query row of this column
+    const int head = g * G + (col_ok[b] ? c % G : 0);
+    pos[b] = T - M + qr;                                      // its position
+    out_row[b] = int64_t(row_begin + min(qr, M - 1)) * a.num_q_heads + head;
+    const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
+                                                       out_row[b] * kRowBytes);
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+      cols[b].qb[kk] = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int n = 0; n < PC::NT; ++n) cols[b].o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    cols[b].m_run = -INFINITY;
+    cols[b].l_run = 0.0f;
+  }
+
+  // the wave's first position; a wave with no queries computes columns it
+  // never stores, so any bound serves it
+  const int first_pos = T - M + rw;
+  const int ntiles = (T - M + r0 + nq_wg - 1) / kTileTokens + 1;   // up to the last position
+  const int nsteps = (ntiles + 1) / 2;                             // 32-key steps
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
+  const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
+  const int64_t head_rows = int64_t(g) << lb;
+  const int64_t blk_rows = int64_t(a.num_kv_heads) << lb;
+  const char* kbase = static_cast<const char*>(a.k_pool);
+  const char* vbase = static_cast<const char*>(a.v_pool);
+  const int nblk = a.num_blocks;
+  // this thread's share of a step: chunk lchunk of step rows lrow + i * kLoadRows,
+  // the rows of one 32-lane pass spread as the LDS layout wants
+  constexpr int kPassRows = 32 / CPR;
+  const int q = threadIdx.x / CPR, lchunk = threadIdx.x % CPR;
+  const int lrow = (q & ~15) + (q & 15) / kPassRows + (16 / kPassRows) * (q % kPassRows);
+  // the tile a load instruction of this wave covers, relative to the step's
+  // first tile (the same for all of the wave's lanes)
+  auto load_half = [&](int i) {
+    return (i * kLoadRows + wave * (kWave / CPR)) / kTileTokens;
+  };
+
+  // tile k's block (one per lane, 64 tiles per load) when tiles lie in blocks
+  int tbl = 0;
+  auto load_tbl = [&](int batch) {
+    const int k = min(64 * batch + lane, ntiles - 1);
+    tbl = min(max(table[(k * kTileTokens) >> lb], 0), nblk - 1);
+  };
+  // the buffer spans the tile's rows below T only; a tile past the last
+  // position (the second half of the last step) spans none: its table lane
+  // holds another tile's block, and it must read as zeros
+  auto rsrc = [&](const char* base, int k) {
+    const int64_t blk = __builtin_amdgcn_readlane(tbl, k & 63);
+    const int64_t byte = (blk * blk_rows + head_rows + ((k * kTileTokens) & bmask)) * kRowBytes;
+    const int rows = k < ntiles ? min(kTileTokens, T - k * kTileTokens) : 0;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + byte), 0,
+                                             rows * kRowBytes, kBufferDword3);
+  };
+  // blocks smaller than a tile: each row finds its block; rows past T - 1
+  // read row T - 1 (weight zero)
+  auto row_of = [&](int t) -> int64_t {
+    t = min(t, T - 1);
+    const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
+    return blk * blk_rows + head_rows + (t & bmask);
+  };
+  struct Stage {
+    uint4 k[kLoads], v[kLoads];
+  };
+  auto load_step = [&](int st, Stage& r) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int sr = i * kLoadRows + lrow;                 // row of the step
+      if constexpr (kTileInBlock) {
+        const int k = 2 * st + load_half(i);
+        const int off = (sr % kTileTokens) * kRowBytes + lchunk * 16;
+        r.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsrc(kbase, k), off, 0, 0));
+        r.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                               rsrc(vbase, k), off, 0, 0));
+      } else {
+        const int64_t row = row_of(st * kStepRows + sr);
+        r.k[i] = reinterpret_cast<const uint4*>(kbase + row * kRowBytes)[lchunk];
+        r.v[i] = reinterpret_cast<const uint4*>(vbase + row * kRowBytes)[lchunk];
+      }
+    }
+  };
+  auto store_step = [&](const Stage& r, char* st) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int sr = i * kLoadRows + lrow;
+      *reinterpret_cast<uint4*>(st + sr * LS::kKeyStride + lchunk * 16) = r.k[i];
+      *reinterpret_cast<uint4*>(st + LS::kValOffset + sr * LS::kValStride + lchunk * 16) =
+          r.v[i];
+    }
+  };
+
+  Stage R;
+  // lane (gq, c) reads value row 4gq + c/4, dimensions 16n + 4(c%4) .. +3 of
+  // each step (a local-memory pointer: stage and constants fold into the
+  // read instructions' offsets)
+  lds_char* const lds_v = (lds_char*)lds + LS::kValOffset +
+                          (4 * gq + (c >> 2)) * LS::kValStride + ((c & 1) << 3) +
+                          (((c & 3) >> 1) << 4);
+  // byte offset of step st's LDS stage, unsigned so that the compiler can
+  // fold each read's constant part into the instruction's offset field
+  auto stage_of = [](int st) -> uint32_t { return uint32_t(st) % kStages * kStageBytes; };
+  // S^T of a step for every column block (keys from the step's LDS stage)
+  using Scores = f32x4[NB][2];
+  auto qk = [&](int st, Scores& sc) {
+    const char* kt = lds + stage_of(st);
+    // lane (gq, c): key row c of each half, chunks 4kk + gq
+    const char* kb = kt + c * LS::kKeyStride + gq * 16;
+    KeyRegs<DT, D> kr[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+        kr[h].k[kk] = *reinterpret_cast<const uint4*>(kb + h * kTileTokens * LS::kKeyStride +
+                                                      64 * kk);
+#pragma unroll
+    for (int b = 0; b < NB; ++b) prefill_qk32<DT, D>(cols[b], kr[0], kr[1], sc[b][0], sc[b][1]);
+  };
+  // Step st: stage the rows of step st + 1 and fetch those of st + 2; after
+  // the barrier, step st + 1's rows are complete too, so its scores go to the
+  // matrix cores before step st's softmax and P.V (`cur` holds step st's
+  // scores, `next` receives step st + 1's).
+  auto step = [&](int st, Scores& cur, Scores& next) {
+    if (st + 1 < nsteps) {
+      store_step(R, lds + stage_of(st + 1));
+      if (st + 2 < nsteps) {
+        if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
+        load_step(st + 2, R);
+      }
+    }
+    __syncthreads();
+    if (st + 1 < nsteps) qk(st + 1, next);
+    // masking is needed unless every key of the step precedes every
+    // column's position
+    const bool mask = (st + 1) * kStepRows - 1 > first_pos;
+    int live[NB][2];
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      // keys at positions 32 st .. pos of this column take part
+      const int before = col_ok[b] ? pos[b] - st * kStepRows + 1 : 0;
+      live[b][0] = min(kTileTokens, max(0, before));
+      live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
+    }
+    prefill_softmax32<DT, D, NB>(cols, a, cur, gq, mask, live);
+    accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
+  };
+
+  if constexpr (kTileInBlock) load_tbl(0);
+  load_step(0, R);
+  store_step(R, lds);
+  if (nsteps > 1) load_step(1, R);
+  __syncthreads();
+  Scores SA, SB;
+  qk(0, SA);
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, SA, SB);
+    if (st + 1 >= nsteps) break;
+    step(st + 1, SB, SA);
+  }
+
+#pragma unroll
+  for (int b = 0; b < NB; ++b) {
+    // column c's sum is spread over its four lanes (gq = 0..3)
+    float l = cols[b].l_run;
+    l += __shfl_xor(l, 16, kWave);
+    l += __shfl_xor(l, 32, kWave);
+    if (col_ok[b]) {
+      const float inv = 1.0f / l;
+#pragma unroll
+      for (int n = 0; n < PC::NT; ++n)
+        store4<DT>(a.out, out_row[b] * D + 16 * n + 4 * gq, cols[b].o[n] * inv);
+    }
+  }
+}
+
+}  // namespace
+
+namespace {
+
+template <int DT, int D, int G>
+hipError_t launch_prefill_g(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (DT == PA_F32) {
+    return hipErrorInvalidValue;
+  } else {
+    const dim3 grid(static_cast<uint32_t>(
+        prefill_workgroups(a.num_seqs, a.num_kv_heads, G, a.max_query_len)));
+    if (a.log2_block >= 4)
+      launch_timed(prefill_kernel<DT, D, G, true>, grid, dim3(kWave * kPrefillWaves), stream, a);
+    else
+      launch_timed(prefill_kernel<DT, D, G, false>, grid, dim3(kWave * kPrefillWaves), stream, a);
+    return hipGetLastError();
+  }
+}
+
+template <int DT, int D>
+hipError_t launch_prefill_d(const DecodeArgs& a, int32_t group, hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_prefill_g<DT, D, 1>(a, stream);
+    case 2: return launch_prefill_g<DT, D, 2>(a, stream);
+    case 3: return launch_prefill_g<DT, D, 3>(a, stream);
+    case 4: return launch_prefill_g<DT, D, 4>(a, stream);
+    case 5: return launch_prefill_g<DT, D, 5>(a, stream);
+    case 6: return launch_prefill_g<DT, D, 6>(a, stream);
+    case 7: return launch_prefill_g<DT, D, 7>(a, stream);
+    case 8: return launch_prefill_g<DT, D, 8>(a, stream);
+    case 16: return launch_prefill_g<DT, D, 16>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int DT>
+hipError_t launch_prefill_dt(const DecodeArgs& a, int32_t head_dim, int32_t group,
+                             hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_prefill_d<DT, 64>(a, group, stream);
+    case 128: return launch_prefill_d<DT, 128>(a, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, int32_t group,
+                          hipStream_t stream) {
+  if (a.num_seqs == 0 || a.max_query_len == 0) return hipSuccess;
+  switch (dtype) {
+    case PA_F16: return launch_prefill_dt<PA_F16>(a, head_dim, group, stream);
+    case PA_BF16: return launch_prefill_dt<PA_BF16>(a, head_dim, group, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace pa
