@@ -124,17 +124,21 @@ PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama3-8b-bf16.j
 COPY_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "copy_blocks_llama3-8b-cow256-bf16.json")
 
 
-def summary_traffic(path, source):
+def summary_traffic(path, sources):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
     summary, or None when the summary does not describe the kernel as built
-    now (it records the sha256 of the kernel's source file)."""
+    now (it records the sha256 of the kernel's source files, concatenated in
+    the order given)."""
     import hashlib
     if not os.path.exists(path):
         return None, None
     with open(path) as f:
         prof = json.load(f)
-    with open(os.path.join(ROOT, "paged_kv_cache_75_amd", "csrc", source), "rb") as f:
-        sha = hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for source in sources:
+        with open(os.path.join(ROOT, "paged_kv_cache_75_amd", "csrc", source), "rb") as f:
+            h.update(f.read())
+    sha = h.hexdigest()
     if sha != prof.get("kernel_source_sha256"):
         return None, None
     return prof["traffic_bytes_per_launch"], prof
@@ -144,7 +148,7 @@ def profiled_traffic(cfg):
     """Traffic of the decode step's attention kernel (configuration 3 only)."""
     if cfg != 3:
         return None, None
-    return summary_traffic(PROFILE_SUMMARY, "pa_kernels.hip")
+    return summary_traffic(PROFILE_SUMMARY, ("pa_device.h", "pa_kernels.hip"))
 
 
 def kv_bytes_per_step(w, window: int = 0) -> int:
@@ -363,7 +367,7 @@ def cow_main(args):
     alloc_us = (time.perf_counter() - t) * 1e6 / 100
 
     achieved = moved / (kernel_us * 1e-6) / 1e9
-    traffic_bytes, _ = summary_traffic(COPY_PROFILE_SUMMARY, "pa_copy.hip") if N == 256 else (None, None)
+    traffic_bytes, _ = summary_traffic(COPY_PROFILE_SUMMARY, ("pa_copy.hip",)) if N == 256 else (None, None)
     result = {
         "metric": "copy-on-write block copy: bytes moved/s (TB/s, read + write), us/step",
         "value": round(moved / (ms * 1e-3) / 1e12, 4),
