@@ -302,6 +302,11 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   // the wave's first position; a wave with no queries computes columns it
   // never stores, so any bound serves it
   const int first_pos = T - M + rw;
+  // steps this wave computes: up to its last query's position (none when it
+  // holds no query rows, e.g. the decode tokens of a mixed batch).  Later
+  // steps are wholly masked for it and would leave its sums unchanged; the
+  // wave still stages rows and meets every barrier.
+  const int wave_steps = nq > 0 ? ((T - M + rw + nq - 1) / kTileTokens + 2) / 2 : 0;
   const int ntiles = (T - M + r0 + nq_wg - 1) / kTileTokens + 1;   // up to the last position
   const int nsteps = (ntiles + 1) / 2;                             // 32-key steps
   const int lb = a.log2_block;
@@ -416,7 +421,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       }
     }
     __syncthreads();
-    if (st + 1 < nsteps) qk(st + 1, next);
+    if (st + 1 < wave_steps) qk(st + 1, next);
+    if (st >= wave_steps) return;
     // masking is needed unless every key of the step precedes every
     // column's position
     const bool mask = (st + 1) * kStepRows - 1 > first_pos;
@@ -438,7 +444,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   if (nsteps > 1) load_step(1, R);
   __syncthreads();
   Scores SA, SB;
-  qk(0, SA);
+  if (wave_steps > 0) qk(0, SA);
   for (int st = 0; st < nsteps; st += 2) {
     step(st, SA, SB);
     if (st + 1 >= nsteps) break;
