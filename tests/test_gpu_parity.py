@@ -457,7 +457,8 @@ def _prefill_case(w, mq, seed, label, sample_rows=None, scale=None):
             compare(got[qs[i]:qs[i + 1]], want, w.dtype, label=f"{label} seq {i}")
 
 
-PREFILL_SHAPES = [("bf16", 16, 4, 128), ("f16", 16, 7, 64), ("f16", 8, 1, 128), ("bf16", 32, 16, 128)]
+PREFILL_SHAPES = [("bf16", 16, 4, 128), ("f16", 16, 7, 64), ("f16", 8, 1, 128), ("bf16", 32, 16, 128),
+                  ("bf16", 256, 8, 64), ("f16", 64, 2, 128)]
 
 
 @pytest.mark.parametrize("dtype,block_size,group,head_dim", PREFILL_SHAPES,
@@ -471,6 +472,17 @@ def test_prefill_mixed_batch(dtype, block_size, group, head_dim):
     w = workloads.random_paged("prefill", dtype, hkv * group, hkv, head_dim, block_size, lens,
                                seed=1800 + group + block_size, spare_frac=0.1)
     _prefill_case(w, mq, 1900 + group, f"{dtype} B={block_size} G={group} D={head_dim}")
+
+
+def test_prefill_whole_prompt():
+    """One 2,000-token prompt as a single chunk (M = T, 63 query blocks, a
+    ragged last block, every block ending on a diagonal step) next to a short
+    chunk, against the oracle on every row."""
+    lens = [2000, 70]
+    mq = [2000, 30]
+    w = workloads.random_paged("prefill-prompt", "bf16", 8, 2, 64, 16, lens, seed=2500,
+                               spare_frac=0.1)
+    _prefill_case(w, mq, 2501, "whole prompt")
 
 
 @pytest.mark.parametrize("scale", [-0.11, 0.0, 0.5])
