@@ -19,9 +19,9 @@ namespace {
 // chunk; a decode token is M = 1).  A workgroup of kPrefillWaves waves takes
 // one (query block, kv head, sequence); each wave holds kBlocks column blocks,
 // each filling the 16 columns of an MFMA operand holding Q^T with 16 / G
-// queries times the G heads of the kv head.  Column c of block b of wave w is
-// query r = (w * kBlocks + b) * 16 / G + c / G of the query block (head
-// c % G) at position T - M + r; key rows after that position get weight zero
+// queries times the G heads of the kv head (integer division).  Column c of
+// block b of wave w is query r = (w * kBlocks + b) * (16 / G) + c / G of the
+// query block (head c % G) at position T - M + r; key rows after that position get weight zero
 // (its per-lane `live` bound).
 //
 // The workgroup walks the keys in 32-key steps up to its last position.  Each
