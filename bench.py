@@ -122,6 +122,7 @@ def cpu_baseline(w, budget_s: float, window: int = 0, fp8_scales=None):
 
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama3-8b-bf16.json")
 COPY_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "copy_blocks_llama3-8b-cow256-bf16.json")
+PREFILL_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "prefill_llama3-8b-chunk512-bf16.json")
 
 
 def summary_traffic(path, sources):
@@ -224,6 +225,8 @@ def prefill_main(args):
     flops = 4 * 32 * 128 * pairs
     kv_bytes = 2 * 8 * 128 * 2 * sum(lens)
     achieved = flops / (kernel_us * 1e-6) / 1e12
+    traffic_bytes, _ = (summary_traffic(PREFILL_PROFILE_SUMMARY, ("pa_device.h", "pa_prefill.hip"))
+                        if M == 512 else (None, None))
     result = {
         "metric": "chunked prefill attention: TFLOP/s (bf16 matrix cores), us/step",
         "value": round(flops / (ms * 1e-3) / 1e12, 3),
@@ -240,7 +243,10 @@ def prefill_main(args):
         "roofline": {"bound": "mfma", "kernel": "prefill_kernel (attention kernel of pa_prefill)",
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": None, "kernel_us_mean": round(kernel_us, 2),
+                     "traffic": None if traffic_bytes is None else round(traffic_bytes),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                     "copy-calibrated)",
+                     "kernel_us_mean": round(kernel_us, 2),
                      "kernel_launches_timed": launches},
     }
     if not args.no_cpu_baseline:
