@@ -145,11 +145,22 @@ def summary_traffic(path, sources):
     return prof["traffic_bytes_per_launch"], prof
 
 
-def profiled_traffic(cfg):
-    """Traffic of the decode step's attention kernel (configuration 3 only)."""
+DECODE_SOURCES = ("pa_device.h", "pa_kernels.hip")
+WINDOW_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_sliding_llama3-8b-w256-bf16.json")
+FP8_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_fp8_llama3-8b-e4m3.json")
+
+
+def profiled_summary(cfg, fused, window, fp8):
+    """The committed counter summary of the attention kernel a bench line
+    measures, for the workloads that were profiled (configuration 3: the
+    appending step, the 256-token window, FP8 pools), else None."""
     if cfg != 3:
-        return None, None
-    return summary_traffic(PROFILE_SUMMARY, ("pa_device.h", "pa_kernels.hip"))
+        return None
+    if fp8:
+        return FP8_PROFILE_SUMMARY
+    if window:
+        return WINDOW_PROFILE_SUMMARY if window == 256 else None
+    return PROFILE_SUMMARY if fused else None
 
 
 def kv_bytes_per_step(w, window: int = 0) -> int:
@@ -577,7 +588,8 @@ def main():
     achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
 
-    traffic_bytes, prof = profiled_traffic(cfg) if not args.window and fused else (None, None)
+    summary = profiled_summary(cfg, fused, args.window, args.fp8)
+    traffic_bytes, prof = summary_traffic(summary, DECODE_SOURCES) if summary else (None, None)
     traffic = None if traffic_bytes is None else round(traffic_bytes)
     result = {
         "metric": "paged decode attention: KV bytes read/s (TB/s), % HBM peak, us/step",
@@ -621,7 +633,7 @@ def main():
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
-            "traffic_source": os.path.relpath(PROFILE_SUMMARY, ROOT) if traffic is not None else None,
+            "traffic_source": os.path.relpath(summary, ROOT) if traffic is not None else None,
             "kernel_us_mean": round(kernel_us, 2),
             "kernel_timing": "HIP start/stop events attached to the kernel's dispatch "
                              "(pa_profile_start / pa_profile_stop), mean over the steps",
