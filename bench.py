@@ -257,6 +257,8 @@ def prefill_main(args):
                      "traffic": None if traffic_bytes is None else round(traffic_bytes),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                      "copy-calibrated)",
+                     "traffic_source": (os.path.relpath(PREFILL_PROFILE_SUMMARY, ROOT)
+                                        if traffic_bytes is not None else None),
                      "kernel_us_mean": round(kernel_us, 2),
                      "kernel_launches_timed": launches},
     }
