@@ -474,6 +474,21 @@ def test_prefill_mixed_batch(dtype, block_size, group, head_dim):
     _prefill_case(w, mq, 1900 + group, f"{dtype} B={block_size} G={group} D={head_dim}")
 
 
+@pytest.mark.parametrize("dtype,block_size,group,head_dim",
+                         [("bf16", 1, 16, 64), ("f16", 2, 3, 128), ("bf16", 4, 4, 64)],
+                         ids=["bf16-B1-G16-D64", "f16-B2-G3-D128", "bf16-B4-G4-D64"])
+def test_prefill_tiny_blocks(dtype, block_size, group, head_dim):
+    """Blocks smaller than a 16-token tile (each row finds its own block),
+    one-token sequences next to long ones, and a chunk whose queries all sit
+    on diagonal steps."""
+    hkv = 2 if group < 16 else 1
+    lens = [1, 1, 300, 64, 97, 33]
+    mq = [1, 1, 40, 64, 1, 33]
+    w = workloads.random_paged("prefill-tiny", dtype, hkv * group, hkv, head_dim, block_size, lens,
+                               seed=2600 + block_size, spare_frac=0.1)
+    _prefill_case(w, mq, 2601 + block_size, f"{dtype} B={block_size} G={group} D={head_dim}")
+
+
 def test_prefill_whole_prompt():
     """One 2,000-token prompt as a single chunk (M = T, 63 query blocks, a
     ragged last block, every block ending on a diagonal step) next to a short
