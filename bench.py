@@ -8,6 +8,8 @@ newest K/V rows go into the pools and the attention reads them, in one call
 (the stream kernel plus the piece merge, which also writes the rows).  The
 same step as two calls, pa_write_kv then pa_decode, is timed beside it and
 reported as "two_call".  Other configurations decode only (pa_decode).
+With --fp8 the pools hold FP8 (E4M3) codes and the step is
+pa_append_decode_fp8 (two calls: pa_write_kv_fp8 then pa_decode_fp8).
 Inputs are resident in HBM before timing starts.  To keep the timed reads
 cold in the GPU caches, steps rotate over several copies of the pools
 (together well above the 256 MB Infinity Cache).
@@ -453,7 +455,8 @@ def main():
     import torch
 
     import workloads
-    from paged_kv_cache_75_amd import (fp8_pool_desc, pa_append_decode, pa_decode,
+    from paged_kv_cache_75_amd import (fp8_pool_desc, pa_append_decode, pa_append_decode_fp8,
+                                       pa_decode,
                                        pa_decode_fp8, pa_decode_sliding,
                                        pa_decode_workspace_bytes, pa_profile_start,
                                        pa_profile_stop, pa_write_kv, pa_write_kv_fp8, pool_desc)
@@ -519,9 +522,13 @@ def main():
                       workspace=ws, partition_tokens=args.partition)
 
     def append_decode(kp, vp):
-        pa_append_decode(q, nk, nv, kp, vp, bt, cl, w.scale, out=out,
-                         max_context_len=w.max_context_len, workspace=ws,
-                         partition_tokens=args.partition)
+        if args.fp8:
+            pa_append_decode_fp8(q, nk, nv, kp, vp, bt, cl, w.scale, ks, vs, out=out,
+                                 max_context_len=w.max_context_len, workspace=ws)
+        else:
+            pa_append_decode(q, nk, nv, kp, vp, bt, cl, w.scale, out=out,
+                             max_context_len=w.max_context_len, workspace=ws,
+                             partition_tokens=args.partition)
 
     def timed(pre, call):
         """Step time: K steps between device synchronisations, nothing else
@@ -572,7 +579,7 @@ def main():
         pass
 
     K = args.steps
-    fused = writes and args.step != "two-call" and not args.window and not args.fp8
+    fused = writes and args.step != "two-call" and not args.window
     two_call = writes and args.step != "append"
     if two_call:
         two_ms, two_decode_ms, two_kernel_us = timed(write, decode)
@@ -619,7 +626,7 @@ def main():
             "new_tokens_written": int((w.slot_mapping >= 0).sum()) if writes else 0,
             "pool_copies_rotated": reps,
             "partition_tokens": args.partition or "auto",
-            "step_calls": ("pa_append_decode" if fused else
+            "step_calls": (("pa_append_decode_fp8" if args.fp8 else "pa_append_decode") if fused else
                            ("pa_write_kv_fp8 + pa_decode_fp8" if args.fp8 else
                             ("pa_write_kv + " if writes else "") +
                             ("pa_decode_sliding" if args.window else "pa_decode"))),
@@ -627,7 +634,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": (attention_kernel + " (attention kernel of " +
-                       ("pa_append_decode" if fused else "pa_decode_fp8" if args.fp8 else
+                       (("pa_append_decode_fp8" if args.fp8 else "pa_append_decode") if fused
+                        else "pa_decode_fp8" if args.fp8 else
                         "pa_decode_sliding" if args.window else "pa_decode") + ")"),
             "achieved": round(achieved, 1),
             "peak": HBM_PEAK_GBS,
@@ -645,7 +653,7 @@ def main():
     }
     if two_call and fused:
         result["two_call"] = {
-            "calls": "pa_write_kv + pa_decode",
+            "calls": "pa_write_kv_fp8 + pa_decode_fp8" if args.fp8 else "pa_write_kv + pa_decode",
             "us_per_step": round(two_ms * 1e3, 2),
             "value": round(kv_bytes / (two_ms * 1e-3) / 1e12, 4),
             "decode_call_us_mean": round(sum(two_decode_ms) / len(two_decode_ms) * 1e3, 2),

@@ -237,6 +237,27 @@ pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                            int32_t partition_tokens, void* stream);
 
 /*
+ * pa_append_decode_fp8 -- pa_append_decode over FP8 pools: every sequence's
+ * newest token is quantized into the pools and attended over, with the same
+ * bits as
+ *   pa_write_kv_fp8(new_k, new_v, slot_mapping, num_seqs, ..., k_scale, v_scale),
+ *   then pa_decode_fp8(...)
+ * (slot_mapping as for pa_append_decode; the FP8 pool format of the vLLM-design
+ * page's engine settings, kv_cache_dtype "fp8", as pa_write_kv_fp8 states it).
+ * new_k, new_v are [num_seqs][num_kv_heads][head_dim] in pool->dtype (fp16 or
+ * bf16, the type of q and out).  Other arguments, the contract on the newest
+ * token's slot and the workspace are those of pa_append_decode and
+ * pa_decode_fp8 (balanced split only, no partition argument).
+ */
+pa_status pa_append_decode_fp8(const void* q, const void* new_k, const void* new_v,
+                               void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_context_len, int32_t num_q_heads, float scale,
+                               float k_scale, float v_scale, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
  * pa_prefill -- causal attention of a prompt chunk through the block table
  * (chunked prefill: "vLLM Framework and Inference Engine Design", scheduler
  * step and "How does it support prompts of arbitrary length?": a long prompt

@@ -5,7 +5,8 @@
     pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, ...)
     pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, window, ...)
     pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, ...)
-    pa_write_kv_fp8 / pa_decode_fp8: the same over FP8 (E4M3) pools with per-pool scales
+    pa_write_kv_fp8 / pa_decode_fp8 / pa_append_decode_fp8: the same over FP8 (E4M3)
+    pools with per-pool scales
     pa_copy_blocks(pools, block_mapping): whole-block copies for copy-on-write
         (pools: a list of tensors or a PoolSet prepared once)
     pa_check_inputs(k_pool, slot_mapping, block_tables, context_lens): report
@@ -19,14 +20,15 @@ missing; nothing falls back to another implementation.
 """
 from .binding import (BlockManager, OutOfBlocks, PoolSet, pa_check_inputs, pa_copy_blocks, pa_sha256, PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED,
                       PA_ERR_WORKSPACE_TOO_SMALL, PA_F16, PA_F32, PA_OK, PaError, lib,
-                      fp8_pool_desc, pa_append_decode, pa_decode, pa_decode_fp8,
+                      fp8_pool_desc, pa_append_decode, pa_append_decode_fp8, pa_decode, pa_decode_fp8,
                       pa_decode_sliding, pa_decode_workspace_bytes, pa_pool_desc, pa_prefill,
                       pa_profile_start, pa_profile_stop, pa_status_string, pa_write_kv,
                       pa_write_kv_fp8, pool_desc)
 
 __all__ = ["BlockManager", "OutOfBlocks", "PoolSet", "pa_check_inputs", "pa_copy_blocks", "pa_sha256", "PA_BF16", "PA_ERR_HIP", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED",
            "PA_ERR_WORKSPACE_TOO_SMALL", "PA_F16", "PA_F32", "PA_OK", "PaError", "lib",
-           "fp8_pool_desc", "pa_append_decode", "pa_decode", "pa_decode_fp8",
+           "fp8_pool_desc", "pa_append_decode", "pa_append_decode_fp8", "pa_decode",
+           "pa_decode_fp8",
            "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_pool_desc", "pa_prefill",
            "pa_profile_start", "pa_profile_stop", "pa_status_string", "pa_write_kv",
            "pa_write_kv_fp8", "pool_desc"]

@@ -83,6 +83,9 @@ def lib():
                             c_int),
         "pa_decode_fp8": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
                            ctypes.c_float, ctypes.c_float, vp, vp, sz, vp], c_int),
+        "pa_append_decode_fp8": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
+                                  ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, sz, vp],
+                                 c_int),
         "pa_profile_start": ([], c_int),
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
@@ -281,6 +284,54 @@ def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale,
                              workspace.numel() * workspace.element_size(), _stream(stream))
     if st != PA_OK:
         raise PaError(st, "pa_decode_fp8")
+    return out
+
+
+def pa_append_decode_fp8(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,
+                         k_scale, v_scale, out=None, max_context_len=None, workspace=None,
+                         stream=None):
+    """Quantize token T_i - 1 of every sequence (rows of new_k / new_v,
+    [N][Hkv][D], q's dtype) into the FP8 pools and decode, in one call; same
+    result as pa_write_kv_fp8 followed by pa_decode_fp8."""
+    torch = _torch()
+    _on_current_device(k_pool, "k_pool")
+    desc = fp8_pool_desc(k_pool, q)
+    dev = k_pool.device
+    _check(k_pool, "k_pool", dtype=torch.uint8, device=dev)
+    _check(v_pool, "v_pool", dtype=torch.uint8, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(q, "q", dim=3, device=dev)
+    _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    n, hq, d = (int(x) for x in q.shape)
+    if d != desc.head_dim:
+        raise ValueError("q head_dim differs from the pool's")
+    if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    want = (n, desc.num_kv_heads, desc.head_dim)
+    for t, name in ((new_k, "new_k"), (new_v, "new_v")):
+        _check(t, name, dtype=q.dtype, device=dev)
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must be {want}")
+    if max_context_len is None:
+        max_context_len = int(context_lens.max().item()) if n else 0
+    if out is None:
+        out = torch.empty_like(q)
+    _check(out, "out", dtype=q.dtype, device=dev)
+    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, 0)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check(workspace, "workspace", device=dev)
+    st = lib().pa_append_decode_fp8(q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(),
+                                    k_pool.data_ptr(), v_pool.data_ptr(), ctypes.byref(desc),
+                                    block_tables.data_ptr(), int(block_tables.shape[1]),
+                                    context_lens.data_ptr(), n, int(max_context_len), hq,
+                                    float(scale), float(k_scale), float(v_scale), out.data_ptr(),
+                                    workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_append_decode_fp8")
     return out
 
 

@@ -177,6 +177,7 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
                                     1.4426950408889634);
   a.kv_fp8 = kv_fp8 ? 1 : 0;
   a.v_scale = kv_fp8 ? v_scale : 1.0f;
+  a.k_scale = kv_fp8 ? k_scale : 1.0f;
   a.new_k = new_k;
   a.new_v = new_v;
   a.window = window;
@@ -246,6 +247,19 @@ pa_status pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
                         float v_scale, void* out, void* workspace, size_t workspace_bytes,
                         void* stream) {
   return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                workspace_bytes, 0, 0, stream, true, k_scale, v_scale);
+}
+
+pa_status pa_append_decode_fp8(const void* q, const void* new_k, const void* new_v,
+                               void* k_pool, void* v_pool, const pa_pool_desc* pool,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t num_seqs,
+                               int32_t max_context_len, int32_t num_q_heads, float scale,
+                               float k_scale, float v_scale, void* out, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (num_seqs > 0 && (!new_k || !new_v)) return PA_ERR_INVALID_ARGUMENT;
+  return decode(q, new_k, new_v, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                 context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
                 workspace_bytes, 0, 0, stream, true, k_scale, v_scale);
 }

@@ -64,6 +64,7 @@ struct DecodeArgs {
   // key scale is folded into scale_log2
   int32_t kv_fp8;
   float v_scale;
+  float k_scale;            // FP8 pools: the key scale itself (appended rows are quantized)
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);

@@ -59,6 +59,15 @@ __global__ __launch_bounds__(256) void write_kv_kernel(WriteArgs a) {
 // with ties to an even mantissa; 448 and above (infinities too) saturate to
 // 448, NaN stays NaN.  Written from the OCP 8-bit floating point definition:
 // 4 exponent bits with bias 7, 3 mantissa bits, S.1111.111 reserved for NaN.
+// a 16-bit element's bits as float (exact)
+template <int DT> __device__ inline float half_bits_to_float(uint32_t h);
+template <> __device__ inline float half_bits_to_float<PA_F16>(uint32_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(h)));
+}
+template <> __device__ inline float half_bits_to_float<PA_BF16>(uint32_t h) {
+  return __uint_as_float(h << 16);
+}
+
 __device__ inline uint32_t e4m3_code(float y) {
   const uint32_t u = __float_as_uint(y);
   const uint32_t sign = (u >> 24) & 0x80;
@@ -896,7 +905,29 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
           (int64_t(sm.seg_seq[sg]) * Hq + int64_t(sm.seg_g[sg]) * G) * kRowBytes);
       *reinterpret_cast<uint4*>(sm.q[sg] + part * 16) = src[part];
     }
-    if constexpr (kAppend) {        // new K row, then new V row, of each segment's pair
+    if constexpr (kAppend && kFp8) {
+      // FP8 pools: each segment's new K and V rows are quantized here as the
+      // FP8 slot write does (the code of x / scale) and kept as codes, which
+      // then take the pool rows' path through the tile math and are the bytes
+      // stored to the slot
+      constexpr int kQuadsPerRow = D / 4;                       // four codes per lane
+      for (int idx = lane; idx < nseg * 2 * kQuadsPerRow; idx += kWave) {
+        const int sg = idx / (2 * kQuadsPerRow);
+        const int part = idx - sg * 2 * kQuadsPerRow;
+        const bool is_v = part >= kQuadsPerRow;
+        const int quad = is_v ? part - kQuadsPerRow : part;
+        const uint2 x = *(reinterpret_cast<const uint2*>(
+                              static_cast<const char*>(is_v ? a.new_v : a.new_k) +
+                              (int64_t(sm.seg_seq[sg]) * Hkv + sm.seg_g[sg]) * kRowBytes) +
+                          quad);
+        const float sc = is_v ? a.v_scale : a.k_scale;
+        const uint32_t h[4] = {x.x & 0xffffu, x.x >> 16, x.y & 0xffffu, x.y >> 16};
+        uint32_t word = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) word |= e4m3_code(half_bits_to_float<DT>(h[e]) / sc) << (8 * e);
+        *reinterpret_cast<uint32_t*>(sm.newkv[sg] + (is_v ? kPoolRowBytes : 0) + 4 * quad) = word;
+      }
+    } else if constexpr (kAppend) {   // new K row, then new V row, of each segment's pair
       for (int idx = lane; idx < nseg * 2 * CPR; idx += kWave) {
         const int sg = idx / (2 * CPR);
         const int part = idx - sg * 2 * CPR;
@@ -986,13 +1017,13 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       const char* nk = sm.newkv[(kr.meta >> 8) & 0xf];
       if (lane == 0)
         sm.new_dst[(kr.meta >> 8) & 0xf] =
-            (kr.meta & kMetaStore) ? kr.off + int64_t(live - 1) * kRowBytes : int64_t(-1);
+            (kr.meta & kMetaStore) ? kr.off + int64_t(live - 1) * kPoolRowBytes : int64_t(-1);
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
         const uint4 x = *reinterpret_cast<const uint4*>(nk + (gq + 4 * kk) * 16);
         if (c == live - 1) kr.r.k[kk] = x;
       }
-      const uint4 y = *reinterpret_cast<const uint4*>(nk + kRowBytes + chi * 16);
+      const uint4 y = *reinterpret_cast<const uint4*>(nk + kPoolRowBytes + chi * 16);
 #pragma unroll
       for (int s2 = 0; s2 < VS; ++s2)
         if (rho + s2 * RPI == live - 1) vr.v[s2] = y;
@@ -1316,20 +1347,31 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
     if constexpr (DT == PA_F32) {
       return hipErrorInvalidValue;
     } else {
-      // variants: appending decode, sliding window, FP8 pools, plain (one at a time)
-      const int mode = a.new_k != nullptr ? 1 : a.window > 0 ? 2 : a.kv_fp8 ? 3 : 0;
+      // variants: appending decode, sliding window, FP8 pools, appending over
+      // FP8 pools, plain (one at a time)
+      const int mode = a.new_k != nullptr ? (a.kv_fp8 ? 4 : 1) : a.window > 0 ? 2 : a.kv_fp8 ? 3 : 0;
       const void* k =
           mode == 1 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true, false, false>)
           : mode == 2 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, true, false>)
           : mode == 3 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, true>)
+          : mode == 4 ? reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, true, false, true>)
                       : reinterpret_cast<const void*>(&decode_stream_kernel<DT, D, G, false, false, false>);
       // The plain, appending and sliding-window variants split the work the
       // same way, so their results agree bit for bit (pa_append_decode equals
       // pa_write_kv + pa_decode): they share one workgroup count, the
-      // smallest any of them keeps resident.
-      const int key = ((DT * 1000 + D) * 100 + G) * 4;
+      // smallest any of them keeps resident.  The two FP8 variants do the
+      // same (pa_append_decode_fp8 equals pa_write_kv_fp8 + pa_decode_fp8).
+      const int key = ((DT * 1000 + D) * 100 + G) * 8;
       int W = resident_workgroups(k, key + mode, kWave);
-      if (mode != 3) {
+      if (mode >= 3) {
+        // FP8 pools, with or without appending: one count for both
+        W = std::min(resident_workgroups(reinterpret_cast<const void*>(
+                                             &decode_stream_kernel<DT, D, G, false, false, true>),
+                                         key + 3, kWave),
+                     resident_workgroups(reinterpret_cast<const void*>(
+                                             &decode_stream_kernel<DT, D, G, true, false, true>),
+                                         key + 4, kWave));
+      } else {
         W = std::min({resident_workgroups(reinterpret_cast<const void*>(
                                               &decode_stream_kernel<DT, D, G, false, false, false>),
                                           key + 0, kWave),
@@ -1349,6 +1391,9 @@ hipError_t launch_decode_g(const DecodeArgs& args, hipStream_t stream) {
                          stream, a);
       else if (mode == 3)
         launch_timed(decode_stream_kernel<DT, D, G, false, false, true>, dim3(W), dim3(kWave),
+                         stream, a);
+      else if (mode == 4)
+        launch_timed(decode_stream_kernel<DT, D, G, true, false, true>, dim3(W), dim3(kWave),
                          stream, a);
       else
         launch_timed(decode_stream_kernel<DT, D, G, false, false, false>, dim3(W), dim3(kWave),

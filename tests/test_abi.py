@@ -206,6 +206,20 @@ def test_decode_fp8_validation(ks, vs, dt, bs, n, want):
     assert got == want
 
 
+@pytest.mark.parametrize("nk,ks,vs,dt,bs,n,want", [
+    (FAKE, 0.0, 0.1, B.PA_BF16, 16, 4, B.PA_ERR_INVALID_ARGUMENT),  # scales must be > 0
+    (None, 0.1, 0.1, B.PA_BF16, 16, 4, B.PA_ERR_INVALID_ARGUMENT),  # new rows required
+    (FAKE, 0.1, 0.1, B.PA_F32, 16, 4, B.PA_ERR_UNSUPPORTED),        # 16-bit queries only
+    (FAKE, 0.1, 0.1, B.PA_BF16, 8, 4, B.PA_ERR_UNSUPPORTED),        # balanced split only
+    (None, 0.1, 0.1, B.PA_F16, 16, 0, B.PA_OK),                     # nothing to do
+])
+def test_append_decode_fp8_validation(nk, ks, vs, dt, bs, n, want):
+    d = desc(bs=bs, dt=dt)
+    got = B.lib().pa_append_decode_fp8(FAKE, nk, nk, FAKE, FAKE, ctypes.byref(d), FAKE, 16, FAKE,
+                                       n, 100, 8, 0.1, ks, vs, FAKE, FAKE, 1 << 26, None)
+    assert got == want
+
+
 @pytest.mark.parametrize("ks,vs,want", [(0.0, 1.0, B.PA_ERR_INVALID_ARGUMENT),
                                         (1.0, -2.0, B.PA_ERR_INVALID_ARGUMENT),
                                         (1.0, float("inf"), B.PA_ERR_INVALID_ARGUMENT)])

@@ -595,6 +595,53 @@ def test_decode_fp8_configs(cfg):
     _fp8_case(w, 4.0 / 448.0, 5.0 / 448.0, f"config {cfg} fp8")
 
 
+def _check_append_fp8(w, k_scale, v_scale, label):
+    """pa_append_decode_fp8 against pa_write_kv_fp8 + pa_decode_fp8 (output
+    bits and pool bytes) and against the oracle."""
+    import torch
+    from paged_kv_cache_75_amd import pa_append_decode_fp8, pa_decode_fp8, pa_write_kv_fp8
+    dw = upload(w, DEV)
+    kc = ref.quantize_fp8(w.k_pool, w.dtype, k_scale)
+    vc = ref.quantize_fp8(w.v_pool, w.dtype, v_scale)
+    kf, vf = torch.from_numpy(kc.copy()).to(DEV), torch.from_numpy(vc.copy()).to(DEV)
+    ks, vs = torch.from_numpy(kc.copy()).to(DEV), torch.from_numpy(vc.copy()).to(DEV)
+    say(f"[fp8 append] {label}: fused call, then write + decode")
+    fused = pa_append_decode_fp8(dw.q, dw.new_k, dw.new_v, kf, vf, dw.block_tables, dw.context_lens,
+                                 dw.scale, k_scale, v_scale, max_context_len=dw.max_context_len)
+    pa_write_kv_fp8(dw.new_k, dw.new_v, dw.slot_mapping, ks, vs, k_scale, v_scale)
+    split = pa_decode_fp8(dw.q, ks, vs, dw.block_tables, dw.context_lens, dw.scale, k_scale,
+                          v_scale, max_context_len=dw.max_context_len)
+    _sync()
+    a, b = to_host(fused, w.dtype), to_host(split, w.dtype)
+    assert np.array_equal(_bytes(a), _bytes(b)), "fused and two-call outputs differ"
+    assert torch.equal(kf, ks) and torch.equal(vf, vs), "fused and two-call pools differ"
+    kq, vq = ref.write_kv_fp8(kc, vc, w.new_k, w.new_v, w.slot_mapping, w.block_size, w.dtype,
+                              k_scale, v_scale, inplace=True)
+    assert np.array_equal(kf.cpu().numpy(), kq) and np.array_equal(vf.cpu().numpy(), vq)
+    want = ref.decode(w.q, kq, vq, w.block_tables, w.context_lens, w.scale, w.dtype,
+                      kv_dtype="fp8e4m3", k_scale=k_scale, v_scale=v_scale)
+    compare(ref.to_float64(a, w.dtype), want, w.dtype, label=label)
+
+
+@pytest.mark.parametrize("cfg", [3, 2, 5])
+def test_append_decode_fp8_configs(cfg):
+    """The FP8 decode step in one call for the Llama-3-8B, Qwen2-0.5B and
+    prefix-shared batches."""
+    w = workloads.make(cfg, seed=2700 + cfg)
+    _check_append_fp8(w, 4.0 / 448.0, 5.0 / 448.0, f"config {cfg} fp8 append")
+
+
+def test_append_decode_fp8_tile_edges():
+    """The newest token alone in its tile, on a tile's last row, mid-tile, in
+    empty sequences; G = 16 and a D = 64, B = 32 fp16 batch."""
+    lens = [1, 16, 17, 32, 0, 33, 5, 300, 2, 257, 0, 48]
+    w = workloads.random_paged("fp8-append", "bf16", 32, 2, 128, 16, lens, seed=2800,
+                               spare_frac=0.1)
+    _check_append_fp8(w, 0.01, 0.02, "fp8 append G=16")
+    w = workloads.random_paged("fp8-append64", "f16", 8, 4, 64, 32, lens, seed=2801)
+    _check_append_fp8(w, 0.03, 0.005, "fp8 append f16 D=64 B=32")
+
+
 def test_decode_fp8_edges():
     """Short and empty sequences, ragged tails, G = 16."""
     lens = [1, 2, 15, 16, 17, 0, 33, 100, 257]
