@@ -68,24 +68,36 @@ template <> __device__ inline float half_bits_to_float<PA_BF16>(uint32_t h) {
   return __uint_as_float(h << 16);
 }
 
-__device__ inline uint32_t e4m3_code(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t sign = (u >> 24) & 0x80;
-  const uint32_t mag = u & 0x7fffffff;
-  if (mag > 0x7f800000) return sign | 0x7f;                  // NaN
-  const float a = __uint_as_float(mag);
-  if (a >= 448.0f) return sign | 0x7e;
-  if (a < 0.015625f)                                          // below 2^-6: multiples of 2^-9
-    return sign | static_cast<uint32_t>(__builtin_rintf(a * 512.0f));   // exact scaling, RNE
-  uint32_t E = (mag >> 23) - 120;                             // (e - 127) + 7, in 1 .. 15
-  uint32_t m = (mag >> 20) & 7;
-  const uint32_t rest = mag & 0xfffff;                        // the 20 bits below m
-  if (rest > 0x80000 || (rest == 0x80000 && (m & 1))) ++m;
-  if (m == 8) {
-    m = 0;
-    ++E;
+// E4M3 (OCP) codes of four floats, packed in a word, the first in the low
+// byte: round to nearest even, magnitudes above 448 (infinity included)
+// saturate to 448, NaN gives code 0x7f with its sign.  The conversion
+// instruction rounds every finite value below 448 exactly so, but does not
+// saturate and sets a NaN's sign differently: magnitudes above 448 are
+// clamped before it and NaN codes are set after it.  (Compared with the
+// definition written out bit by bit over every float bit pattern: no
+// difference.)
+__device__ inline float e4m3_clamp(float y) {
+  const uint32_t u = __float_as_uint(y), mag = u & 0x7fffffffu;
+  return (mag > 0x43e00000u && mag <= 0x7f800000u)
+             ? __uint_as_float((u & 0x80000000u) | 0x43e00000u)
+             : y;
+}
+__device__ inline uint32_t e4m3_codes4(float y0, float y1, float y2, float y3) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  const v2s zero = {0, 0};
+  const v2s lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(zero, e4m3_clamp(y0), e4m3_clamp(y1),
+                                                          1.0f, false);
+  const v2s all = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(lo, e4m3_clamp(y2), e4m3_clamp(y3),
+                                                           1.0f, true);
+  uint32_t w = __builtin_bit_cast(uint32_t, all);
+  const float y[4] = {y0, y1, y2, y3};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const uint32_t u = __float_as_uint(y[e]);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+      w = (w & ~(0xffu << (8 * e))) | ((((u >> 24) & 0x80u) | 0x7fu) << (8 * e));
   }
-  return sign | (E << 3) | m;                                 // a < 448 keeps this finite
+  return w;
 }
 
 // Slot write into FP8 pools: one workgroup per new token, four elements per
@@ -108,7 +120,7 @@ __global__ __launch_bounds__(256) void write_kv_fp8_kernel(WriteArgs a, float k_
     const int64_t src = (int64_t(n) * a.num_kv_heads + h) * D + e0;
     const void* x = is_v ? a.v : a.k;
     const float scale = is_v ? v_scale : k_scale;
-    uint32_t word = 0;
+    float y[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float f;
@@ -119,8 +131,9 @@ __global__ __launch_bounds__(256) void write_kv_fp8_kernel(WriteArgs a, float k_
       } else {
         f = __uint_as_float(uint32_t(static_cast<const uint16_t*>(x)[src + e]) << 16);
       }
-      word |= e4m3_code(f / scale) << (8 * e);
+      y[e] = f / scale;
     }
+    const uint32_t word = e4m3_codes4(y[0], y[1], y[2], y[3]);
     char* dst = static_cast<char*>(is_v ? a.v_pool : a.k_pool) +
                 ((blk * a.num_kv_heads + h) << a.log2_block | off) * D + e0;
     *reinterpret_cast<uint32_t*>(dst) = word;
@@ -907,7 +920,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     }
     if constexpr (kAppend && kFp8) {
       // FP8 pools: each segment's new K and V rows are quantized here as the
-      // FP8 slot write does (the code of x / scale) and kept as codes, which
+      // FP8 slot write does (the codes of x / scale) and kept as codes, which
       // then take the pool rows' path through the tile math and are the bytes
       // stored to the slot
       constexpr int kQuadsPerRow = D / 4;                       // four codes per lane
@@ -922,9 +935,9 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
                           quad);
         const float sc = is_v ? a.v_scale : a.k_scale;
         const uint32_t h[4] = {x.x & 0xffffu, x.x >> 16, x.y & 0xffffu, x.y >> 16};
-        uint32_t word = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) word |= e4m3_code(half_bits_to_float<DT>(h[e]) / sc) << (8 * e);
+        const uint32_t word =
+            e4m3_codes4(half_bits_to_float<DT>(h[0]) / sc, half_bits_to_float<DT>(h[1]) / sc,
+                        half_bits_to_float<DT>(h[2]) / sc, half_bits_to_float<DT>(h[3]) / sc);
         *reinterpret_cast<uint32_t*>(sm.newkv[sg] + (is_v ? kPoolRowBytes : 0) + 4 * quad) = word;
       }
     } else if constexpr (kAppend) {   // new K row, then new V row, of each segment's pair
