@@ -52,8 +52,9 @@ def parse():
     ap.add_argument("--seed", type=int, default=None)
     ap.add_argument("--partition", type=int, default=0, help="partition tokens (0 = library choice)")
     ap.add_argument("--step", choices=("both", "append", "two-call"), default="both",
-                    help="where the batch writes new tokens: time pa_append_decode (headline) "
-                         "and pa_write_kv + pa_decode (both), or only one of them")
+                    help="where the batch writes new tokens: time the one-call step "
+                         "(pa_append_decode, or pa_append_decode_fp8 with --fp8; the headline) "
+                         "and the two calls (both), or only one of them")
     ap.add_argument("--window", type=int, default=0,
                     help="sliding window in tokens (pa_decode_sliding; 0 = full attention)")
     ap.add_argument("--prefill", type=int, default=0,
@@ -64,7 +65,8 @@ def parse():
                          "this many shared blocks in all 64 pools of Llama-3-8B (32 layers, K "
                          "and V), plus the host block manager's cost for the same batch")
     ap.add_argument("--fp8", action="store_true",
-                    help="FP8 (E4M3) pools with per-pool scales: pa_write_kv_fp8 + pa_decode_fp8")
+                    help="FP8 (E4M3) pools with per-pool scales: pa_append_decode_fp8 (two calls: "
+                         "pa_write_kv_fp8 + pa_decode_fp8)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
