@@ -1,0 +1,28 @@
+"""bench.py's command line on a machine without a GPU: asking for more than
+one GPU is refused with a JSON message and exit status 2 before anything
+touches a device, and --help lists every row's mode."""
+import json
+import os
+import subprocess
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _run(*args):
+    return subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                          capture_output=True, text=True, timeout=300, cwd=ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = _run("--gpus", "2")
+    assert r.returncode == 2
+    line = json.loads(r.stdout.strip().splitlines()[-1])
+    assert line["n_gpus"] == 2 and "one GPU" in line["error"]
+
+
+def test_help_names_every_mode():
+    r = _run("--help")
+    assert r.returncode == 0
+    for flag in ("--prefill", "--window", "--fp8", "--cow", "--step", "--copy-calibration"):
+        assert flag in r.stdout
