@@ -69,6 +69,8 @@ def parse():
                          "pa_write_kv_fp8 + pa_decode_fp8)")
     ap.add_argument("--replicas", type=int, default=0, help="pool copies to rotate (0 = auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-ceiling", action="store_true",
+                    help="skip the streaming-read ceiling (pa_stream_read of 2 GiB) in the line")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 512 MiB buffer 10 times (reference for the "
@@ -90,38 +92,87 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes_per_launch": n, "launches": 10}), flush=True)
 
 
-def cpu_baseline(w, budget_s: float, window: int = 0, fp8_scales=None):
-    """The oracle as it stands (write, then decode), on the same host arrays,
-    one BLAS thread; repeated over growing sequence samples until the budget
-    is spent.  Returns TB/s of KV bytes read, the sample description, cores."""
+# State the oracle workers read: set in the parent before the pool forks, so
+# the children share the arrays (copy-on-write) instead of receiving copies.
+_ORACLE = {}
+
+
+def _oracle_rows(seqs):
+    """Worker: the oracle's decode of some sequences (their output rows)."""
+    import oracle.paged_attention_ref as ref
+    st = _ORACLE
+    w = st["w"]
+    out = ref.decode(w.q, st["k"], st["v"], w.block_tables, w.context_lens, w.scale, w.dtype,
+                     seqs=seqs, window=st["window"] or None,
+                     kv_dtype="fp8e4m3" if st["fp8"] else None,
+                     k_scale=st["fp8"][0] if st["fp8"] else 1.0,
+                     v_scale=st["fp8"][1] if st["fp8"] else 1.0)
+    return out[seqs]
+
+
+def _oracle_write(w, fp8_scales, kc=None, vc=None):
+    import oracle.paged_attention_ref as ref
+    if fp8_scales:
+        return ref.write_kv_fp8(kc, vc, w.new_k, w.new_v, w.slot_mapping, w.block_size, w.dtype,
+                                *fp8_scales)
+    return ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size)
+
+
+def cpu_baseline(w, budget_s: float, kv_bytes: int, window: int = 0, fp8_scales=None):
+    """The oracle as it stands (the slot write, then the decode), on the same
+    host arrays.  All cores: each step's decode is spread over a pool of
+    processes (one BLAS thread each), forked before the GPU is touched; steps
+    repeat until half the budget is spent.  One core: the same code on one
+    process over a sample of whole sequences for the other half.  Returns
+    (TB/s all cores, cores, TB/s one core, sample description)."""
+    import multiprocessing as mp
+
     import numpy as np
 
     import oracle.paged_attention_ref as ref
     from threadpoolctl import threadpool_limits
-    bytes_done, secs, reps = 0, 0.0, 0
     n = w.num_seqs
+    kc = vc = None
     if fp8_scales:
         kc = ref.quantize_fp8(w.k_pool, w.dtype, fp8_scales[0])
         vc = ref.quantize_fp8(w.v_pool, w.dtype, fp8_scales[1])
     with threadpool_limits(1):
-        while secs < budget_s and reps < 100:
+        k, v = _oracle_write(w, fp8_scales, kc, vc)
+    _ORACLE.update(w=w, k=k, v=v, window=window, fp8=fp8_scales)
+    cores = max(1, min(16, len(os.sched_getaffinity(0)), n))
+    # about equal work per task: sequences dealt out longest first
+    order = np.argsort(-np.asarray(w.context_lens), kind="stable")
+    tasks = [np.sort(order[i::cores * 2]) for i in range(cores * 2)]
+    tasks = [t for t in tasks if len(t)]
+    steps, secs = 0, 0.0
+    with threadpool_limits(1):
+        ctx = mp.get_context("fork")
+        with ctx.Pool(cores) as pool:
+            pool.map(_oracle_rows, tasks[:cores])            # workers up
+            while secs < budget_s / 2 and steps < 50:
+                t0 = time.perf_counter()
+                _oracle_write(w, fp8_scales, kc, vc)
+                pool.map(_oracle_rows, tasks)
+                secs += time.perf_counter() - t0
+                steps += 1
+        all_tbps = kv_bytes * steps / secs / 1e12
+        # one core: whole sequences until the other half of the budget is spent
+        done_bytes, one_secs, done = 0, 0.0, 0
+        per_token = kv_bytes / max(1, int(np.minimum(w.context_lens, window or 1 << 62).sum()))
+        rng = np.random.default_rng(0)
+        for i in rng.permutation(n):
             t0 = time.perf_counter()
-            if fp8_scales:
-                k, v = ref.write_kv_fp8(kc, vc, w.new_k, w.new_v, w.slot_mapping, w.block_size,
-                                        w.dtype, *fp8_scales)
-                ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
-                           seqs=np.arange(n), kv_dtype="fp8e4m3", k_scale=fp8_scales[0],
-                           v_scale=fp8_scales[1])
-            else:
-                k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping,
-                                    w.block_size)
-                ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype,
-                           seqs=np.arange(n), window=window or None)
-            secs += time.perf_counter() - t0
-            bytes_done += kv_bytes_per_step(w, window) // (w.elem_bytes if fp8_scales else 1)
-            reps += 1
-    sample = f"{reps} full steps of the same batch (write + decode, all {n} seqs), {secs:.1f} s"
-    return bytes_done / secs / 1e12, sample, 1
+            _oracle_rows(np.array([i]))
+            one_secs += time.perf_counter() - t0
+            done_bytes += per_token * min(int(w.context_lens[i]), window or 1 << 62)
+            done += 1
+            if one_secs >= budget_s / 2:
+                break
+    one_tbps = done_bytes / one_secs / 1e12
+    sample = (f"all cores: {steps} full steps (write + decode of all {n} sequences) in "
+              f"{secs:.1f} s over {cores} processes; one core: the decode of {done} of the "
+              f"{n} sequences in {one_secs:.1f} s")
+    return all_tbps, cores, one_tbps, sample
 
 
 PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama3-8b-bf16.json")
@@ -176,6 +227,19 @@ def kv_bytes_per_step(w, window: int = 0) -> int:
     if window:
         lens = np.minimum(lens, window)
     return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * int(lens.sum())
+
+
+def unique_kv_bytes(w, window: int = 0) -> int:
+    """KV bytes of the distinct pool rows a step attends over: a row that
+    several sequences reach through shared blocks counts once."""
+    import numpy as np
+    rows = set()
+    B = w.block_size
+    for i, T in enumerate(w.context_lens.astype(int)):
+        first = max(0, T - window) if window else 0
+        t = np.arange(first, T)
+        rows.update((w.block_tables[i, t // B].astype(np.int64) * B + t % B).tolist())
+    return 2 * w.num_kv_heads * w.head_dim * w.elem_bytes * len(rows)
 
 
 def prefill_main(args):
@@ -458,12 +522,14 @@ def main():
 
     import workloads
     from paged_kv_cache_75_amd import (fp8_pool_desc, pa_append_decode, pa_append_decode_fp8,
-                                       pa_decode,
-                                       pa_decode_fp8, pa_decode_sliding,
-                                       pa_decode_workspace_bytes, pa_profile_start,
-                                       pa_profile_stop, pa_write_kv, pa_write_kv_fp8, pool_desc)
+                                       pa_decode, pa_decode_fp8, pa_decode_partitioned,
+                                       pa_decode_partitioned_workspace_bytes, pa_decode_sliding,
+                                       pa_profile_start, pa_profile_stop, pa_stream_read,
+                                       pa_write_kv, pa_write_kv_fp8, pool_desc)
 
-    if not torch.cuda.is_available():
+    # torch.cuda.device_count() does not start the GPU runtime: the oracle's
+    # worker processes below are forked before anything touches the GPU
+    if torch.cuda.device_count() < 1:
         sys.exit("bench.py needs a GPU")
     if args.prefill:
         prefill_main(args)
@@ -471,11 +537,17 @@ def main():
     if args.cow:
         cow_main(args)
         return
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     cfg = args.config
     seed = cfg if args.seed is None else args.seed
     w = workloads.make(cfg, seed=seed, poison=False)
+    ks = vs = 4.0 / 448.0              # FP8 pools: about +-4 maps to the top of E4M3
+    kv_bytes = kv_bytes_per_step(w, args.window) // (w.elem_bytes if args.fp8 else 1)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, args.cpu_seconds, kv_bytes, args.window,
+                           (ks, vs) if args.fp8 else None)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
 
     def up(a, dt):
         a = np.ascontiguousarray(a)
@@ -489,7 +561,6 @@ def main():
     slots = up(w.slot_mapping.astype(np.int32), None)
     nk, nv = up(w.new_k, w.dtype), up(w.new_v, w.dtype)
     k0, v0 = up(w.k_pool, w.dtype), up(w.v_pool, w.dtype)
-    ks = vs = 4.0 / 448.0              # FP8 pools: about +-4 maps to the top of E4M3
     if args.fp8:
         # every slot of the pools quantized on the GPU by the slot write
         nb, hkv, bsz, hd = (int(x) for x in k0.shape)
@@ -506,8 +577,8 @@ def main():
     pools = [(k0, v0)] + [(k0.clone(), v0.clone()) for _ in range(reps - 1)]
     out = torch.empty_like(q)
     desc = fp8_pool_desc(k0, q) if args.fp8 else pool_desc(k0)
-    ws_bytes = pa_decode_workspace_bytes(w.num_seqs, w.num_q_heads, desc, w.max_context_len,
-                                         args.partition)
+    ws_bytes = pa_decode_partitioned_workspace_bytes(w.num_seqs, w.num_q_heads, desc,
+                                                     w.max_context_len, args.partition)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     writes = cfg in (3, 5)
 
@@ -519,9 +590,12 @@ def main():
             pa_decode_sliding(q, kp, vp, bt, cl, w.scale, args.window, out=out,
                               max_context_len=w.max_context_len, workspace=ws,
                               partition_tokens=args.partition)
+        elif args.partition:
+            pa_decode_partitioned(q, kp, vp, bt, cl, w.scale, args.partition, out=out,
+                                  max_context_len=w.max_context_len, workspace=ws)
         else:
             pa_decode(q, kp, vp, bt, cl, w.scale, out=out, max_context_len=w.max_context_len,
-                      workspace=ws, partition_tokens=args.partition)
+                      workspace=ws)
 
     def append_decode(kp, vp):
         if args.fp8:
@@ -569,7 +643,21 @@ def main():
         torch.cuda.synchronize()
         launches, kernel_us = pa_profile_stop()
         assert launches == args.steps, (launches, args.steps)
-        return (t1 - t0) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in ev], kernel_us
+        # warm: the same steps on one copy of the pools, back to back (what the
+        # 256 MB Infinity Cache holds of them is then read from it)
+        kp, vp = pools[0]
+        for _ in range(3):
+            pre(kp, vp)
+            call(kp, vp)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            pre(kp, vp)
+            call(kp, vp)
+        torch.cuda.synchronize()
+        warm_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+        return ((t1 - t0) * 1e3 / args.steps, [a.elapsed_time(b) for a, b in ev], kernel_us,
+                warm_ms)
 
     def write(kp, vp):
         if args.fp8:
@@ -584,19 +672,47 @@ def main():
     fused = writes and args.step != "two-call" and not args.window
     two_call = writes and args.step != "append"
     if two_call:
-        two_ms, two_decode_ms, two_kernel_us = timed(write, decode)
+        two_ms, two_decode_ms, two_kernel_us, two_warm_ms = timed(write, decode)
     if fused:
-        ms_per_step, decode_ms, kernel_us = timed(nothing, append_decode)
+        ms_per_step, decode_ms, kernel_us, warm_ms = timed(nothing, append_decode)
     elif writes:
-        ms_per_step, decode_ms, kernel_us = two_ms, two_decode_ms, two_kernel_us
+        ms_per_step, decode_ms, kernel_us, warm_ms = two_ms, two_decode_ms, two_kernel_us, two_warm_ms
     else:
-        ms_per_step, decode_ms, kernel_us = timed(nothing, decode)
+        ms_per_step, decode_ms, kernel_us, warm_ms = timed(nothing, decode)
 
-    kv_bytes = kv_bytes_per_step(w, args.window) // (w.elem_bytes if args.fp8 else 1)
+    # the measured read ceiling: one streaming read of 2 GiB, timed like the
+    # attention kernel (events attached to its dispatch), best of 10
+    ceiling = None
+    if not args.no_read_ceiling:
+        buf = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+        buf.fill_(7)
+        sink = torch.zeros(4, dtype=torch.int32, device=dev)
+        for _ in range(3):
+            pa_stream_read(buf, sink)
+        runs = []
+        for _ in range(10):
+            pa_profile_start()
+            pa_stream_read(buf, sink)
+            torch.cuda.synchronize()
+            runs.append(pa_profile_stop()[1])
+        del buf
+        ceiling = {"TBps": round((2 << 30) / (min(runs) * 1e-6) / 1e12, 4),
+                   "TBps_median": round((2 << 30) / (float(np.median(runs)) * 1e-6) / 1e12, 4),
+                   "bytes": 2 << 30,
+                   "kernel": "stream_read_kernel (pa_stream_read: every byte read once, "
+                             "16-byte non-temporal loads, four in flight per thread)"}
+
     balanced = args.partition == 0 and w.dtype != "f32" and w.block_size >= 16 and w.num_seqs <= 1024
     attention_kernel = "decode_stream_kernel" if balanced else "decode_partition_kernel"
     decode_ms_mean = sum(decode_ms) / len(decode_ms)
-    achieved = kv_bytes / (kernel_us * 1e-6) / 1e9
+    call_us = np.array(decode_ms) * 1e3
+    # bytes the HBM must supply: a block shared by several sequences (a
+    # common prefix) is one block of memory, read once per kv head however
+    # many sequences attend over it; the metric's KV bytes count it once per
+    # sequence (the "effective" rate)
+    unique_bytes = unique_kv_bytes(w, args.window) // (w.elem_bytes if args.fp8 else 1)
+    roof_bytes = unique_bytes if unique_bytes < kv_bytes else kv_bytes
+    achieved = roof_bytes / (kernel_us * 1e-6) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
 
     summary = profiled_summary(cfg, fused, args.window, args.fp8)
@@ -625,6 +741,7 @@ def main():
             "sum_context_tokens": int(w.context_lens.sum()),
             "max_context_len": w.max_context_len,
             "kv_bytes_per_step": kv_bytes,
+            "kv_bytes_unique_per_step": unique_bytes,
             "new_tokens_written": int((w.slot_mapping >= 0).sum()) if writes else 0,
             "pool_copies_rotated": reps,
             "partition_tokens": args.partition or "auto",
@@ -643,6 +760,10 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "bytes": "unique KV bytes (each shared block once)" if roof_bytes < kv_bytes
+                     else "KV bytes",
+            "frac_of_read_ceiling": (round(achieved / (ceiling["TBps"] * 1e3), 4)
+                                     if ceiling else None),
             "traffic": traffic,
             "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, copy-calibrated)",
             "traffic_source": os.path.relpath(summary, ROOT) if traffic is not None else None,
@@ -650,9 +771,21 @@ def main():
             "kernel_timing": "HIP start/stop events attached to the kernel's dispatch "
                              "(pa_profile_start / pa_profile_stop), mean over the steps",
             "call_us_mean": round(decode_ms_mean * 1e3, 2),
+            "call_us_median": round(float(np.median(call_us)), 2),
+            "call_us_p10": round(float(np.percentile(call_us, 10)), 2),
+            "call_us_p90": round(float(np.percentile(call_us, 90)), 2),
             "call_TBps": round(kv_bytes / (decode_ms_mean * 1e-3) / 1e12, 4),
         },
+        "warm": {"us_per_step": round(warm_ms * 1e3, 2),
+                 "value": round(kv_bytes / (warm_ms * 1e-3) / 1e12, 4),
+                 "note": "one copy of the pools, steps back to back (the timed steps above "
+                         f"rotate over {reps} copies, cold in the 256 MB Infinity Cache)"},
+        "read_ceiling": ceiling,
     }
+    if roof_bytes < kv_bytes:
+        result["value_is"] = ("effective: KV bytes counted once per sequence that attends over "
+                              "them; shared prefix blocks are read from memory once per kv head")
+        result["unique_TBps"] = round(unique_bytes / (ms_per_step * 1e-3) / 1e12, 4)
     if two_call and fused:
         result["two_call"] = {
             "calls": "pa_write_kv_fp8 + pa_decode_fp8" if args.fp8 else "pa_write_kv + pa_decode",
@@ -661,11 +794,11 @@ def main():
             "decode_call_us_mean": round(sum(two_decode_ms) / len(two_decode_ms) * 1e3, 2),
             "kernel_us_mean": round(two_kernel_us, 2),
         }
-    if not args.no_cpu_baseline:
-        v, sample, cores = cpu_baseline(w, args.cpu_seconds, args.window,
-                                        (ks, vs) if args.fp8 else None)
-        result["cpu_baseline"] = {"value": round(v, 6), "unit": "TB/s", "cores": cores,
-                                  "kind": "oracle", "sample": sample}
+    if cpu is not None:
+        all_tbps, cores, one_tbps, sample = cpu
+        result["cpu_baseline"] = {"value": round(all_tbps, 6), "unit": "TB/s", "cores": cores,
+                                  "kind": "oracle", "sample": sample,
+                                  "one_core_value": round(one_tbps, 6)}
     print(json.dumps(result), flush=True)
 
 

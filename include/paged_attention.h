@@ -93,15 +93,15 @@ pa_status pa_write_kv(const void* k, const void* v, const int32_t* slot_mapping,
 
 /*
  * pa_decode_workspace_bytes -- size in bytes of the scratch buffer pa_decode
- * needs for these sizes and this partition_tokens (see pa_decode).  With
- * partition_tokens == 0, a 16-bit dtype, block_size >= 16 and num_seqs <= 1024
- * the size depends only on the query heads per kv head and head_dim.  0 means no workspace is needed (a
- * fixed partition longer than every sequence), and workspace may be NULL.
- * Returns 0 also for invalid sizes (pa_decode reports those).
+ * needs for these sizes (see pa_decode).  For fp16/bf16 pools with
+ * block_size >= 16 and num_seqs <= 1024 (the balanced split) the size depends
+ * only on the query heads per kv head and head_dim; otherwise it is that of
+ * fixed 256-token partitions.  0 means no workspace is needed, and workspace
+ * may then be NULL.  Returns 0 also for invalid sizes (pa_decode reports
+ * those).  Host scalars only; nothing is enqueued.
  */
 size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                 const pa_pool_desc* pool, int32_t max_context_len,
-                                 int32_t partition_tokens);
+                                 const pa_pool_desc* pool, int32_t max_context_len);
 
 /*
  * pa_decode -- one decode step of paged attention for num_seqs sequences.
@@ -122,22 +122,19 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  *   scale         multiplies q . k before the softmax (1/sqrt(head_dim) for
  *                 standard attention).
  *   out           [num_seqs][num_q_heads][head_dim], rounded to nearest even.
- *   workspace     float32 scratch of at least pa_decode_workspace_bytes(...)
- *                 bytes for the same sizes and partition_tokens; its contents
- *                 on entry do not matter.  Calls sharing one workspace must be
- *                 ordered on one stream.
- *   partition_tokens  how the context is split across workgroups:
- *                 0  -- the library's choice: for fp16/bf16 pools with a
- *                       block size of at least 16, the flattened work of all
- *                       (sequence, kv head) pairs, in 16-token tiles, is cut
- *                       into equal contiguous shares, one per resident wave
- *                       (at most 1024 sequences); otherwise fixed 256-token
- *                       partitions;
- *                 >0 -- fixed context partitions of that many tokens (a
- *                       multiple of 16, at most 8192).
- *                 Pieces of a pair computed by different workgroups are
- *                 merged by log-sum-exp in a second kernel; the result does
- *                 not depend on the split beyond float32 rounding.
+ *   workspace     scratch of at least pa_decode_workspace_bytes(...) bytes
+ *                 for the same sizes, 16-byte aligned; its contents on entry
+ *                 do not matter.  Calls sharing one workspace must be ordered
+ *                 on one stream.
+ *
+ * How the context is split across workgroups is the library's choice: for
+ * fp16/bf16 pools with a block size of at least 16, the flattened work of all
+ * (sequence, kv head) pairs, in 16-token tiles, is cut into equal contiguous
+ * shares, one per resident wave (at most 1024 sequences); otherwise fixed
+ * 256-token partitions (pa_decode_partitioned with 256).  Pieces of a pair
+ * computed by different workgroups are merged by log-sum-exp in a second
+ * kernel; the split depends only on the sizes and context_lens, so a call
+ * repeated on the same inputs gives the same bits.
  *
  * Supported: head_dim 64 or 128; query heads per kv head 1..8 or 16.
  */
@@ -146,7 +143,34 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t max_blocks_per_seq, const int32_t* context_lens,
                     int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
-                    int32_t partition_tokens, void* stream);
+                    void* stream);
+
+/*
+ * pa_decode_partitioned -- pa_decode with fixed context partitions: every
+ * sequence's context is cut into partitions of partition_tokens tokens (a
+ * multiple of 16, 16 .. 8192); one workgroup attends over one partition of
+ * one (sequence, kv head) pair, and a sequence longer than one partition is
+ * merged by a log-sum-exp reduce kernel (split-K).  Same result as pa_decode
+ * up to float32 rounding.  Every other argument and the error behaviour are
+ * pa_decode's; partition_tokens <= 0 returns PA_ERR_INVALID_ARGUMENT, a value
+ * not a multiple of 16 PA_ERR_INVALID_ARGUMENT, above 8192 PA_ERR_UNSUPPORTED.
+ *
+ * pa_decode_partitioned_workspace_bytes -- its workspace size: one float32
+ * record of head_dim + 2 values per (sequence, query head, partition of the
+ * longest context), 0 when max_context_len fits one partition.  Returns 0
+ * for invalid sizes.  (With partition_tokens 0 it equals
+ * pa_decode_workspace_bytes, which also sizes pa_append_decode and
+ * pa_decode_sliding with partition_tokens 0.)
+ */
+pa_status pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
+                                const pa_pool_desc* pool, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                                float scale, void* out, void* workspace, size_t workspace_bytes,
+                                int32_t partition_tokens, void* stream);
+size_t pa_decode_partitioned_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                             const pa_pool_desc* pool, int32_t max_context_len,
+                                             int32_t partition_tokens);
 
 /*
  * pa_decode_sliding -- pa_decode for a layer trained with sliding-window
@@ -162,8 +186,14 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
  *                 (at most ceil(W / B) + 1 per sequence); entries before them
  *                 may hold anything, e.g. -1 for released blocks.
  *
- * Every other argument, the workspace query and the error behaviour are those
- * of pa_decode.  window < 1 returns PA_ERR_INVALID_ARGUMENT.
+ *   partition_tokens  0: the library's split, as pa_decode; > 0: fixed
+ *                 partitions of that many tokens, as pa_decode_partitioned
+ *                 (partitions start at the tile holding the window's first
+ *                 position).  Workspace: pa_decode_partitioned_workspace_bytes
+ *                 with the same partition_tokens.
+ *
+ * Every other argument and the error behaviour are those of pa_decode.
+ * window < 1 returns PA_ERR_INVALID_ARGUMENT.
  */
 pa_status pa_decode_sliding(const void* q, const void* k_pool, const void* v_pool,
                             const pa_pool_desc* pool, const int32_t* block_tables,
@@ -225,8 +255,10 @@ pa_status pa_decode_fp8(const void* q, const void* k_pool, const void* v_pool,
  * balanced split the decode takes the newest rows straight from new_k / new_v
  * and the workgroup that attends over a sequence's last tile also stores
  * them, so the step is two kernels instead of three; with fixed partitions
- * the rows are written first and the decode follows.  Workspace:
- * pa_decode_workspace_bytes.
+ * the rows are written first and the decode follows.  partition_tokens: 0
+ * for the library's split (as pa_decode), > 0 for fixed partitions (as
+ * pa_decode_partitioned).  Workspace: pa_decode_partitioned_workspace_bytes
+ * with the same partition_tokens.
  */
 pa_status pa_append_decode(const void* q, const void* new_k, const void* new_v,
                            void* k_pool, void* v_pool, const pa_pool_desc* pool,
@@ -366,11 +398,11 @@ pa_status pa_check_inputs(const int32_t* slot_mapping, int32_t num_tokens,
 /*
  * pa_profile_start / pa_profile_stop -- kernel timing for measurements; not
  * needed to compute anything.  Between the two calls, every pa_decode,
- * pa_append_decode, pa_decode_sliding and pa_prefill call launches its
- * attention kernel (the balanced-split stream kernel, the fixed-partition
- * kernel, or the prefill kernel), and every pa_copy_blocks launch, with a
- * HIP start and stop event attached to that dispatch; the piece merge is not
- * included.  pa_profile_stop
+ * pa_decode_partitioned, pa_append_decode, pa_decode_sliding, the FP8 decode
+ * calls and pa_prefill launch their attention kernel (the balanced-split
+ * stream kernel, the fixed-partition kernel, or the prefill kernel), and every
+ * pa_copy_blocks and pa_stream_read launch, with a HIP start and stop event
+ * attached to that dispatch; the piece merge is not included.  pa_profile_stop
  * turns timing off, waits for the recorded events, and returns how many
  * launches were timed and their mean duration in microseconds (0 launches:
  * mean 0).  The switch is process-wide; while it is on each call creates two
@@ -378,6 +410,18 @@ pa_status pa_check_inputs(const int32_t* slot_mapping, int32_t num_tokens,
  */
 pa_status pa_profile_start(void);
 pa_status pa_profile_stop(int32_t* launches, double* mean_us);
+
+/*
+ * pa_stream_read -- read `bytes` bytes of a device buffer once, 16 bytes per
+ * load with several loads in flight per thread (a measurement helper, not part
+ * of the computation: the read ceiling that the decode kernels' KV bandwidth is
+ * set against).  buf is 16-byte aligned and bytes a multiple of 16 (else
+ * PA_ERR_INVALID_ARGUMENT); sink is a device uint32, written only when the
+ * data match a fixed 32-bit hash (it exists so that no load can be dropped).
+ * Its launch is timed by pa_profile_start / pa_profile_stop like the attention
+ * kernels.
+ */
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 /* Human-readable name of a status code (static storage, never NULL). */
 const char* pa_status_string(pa_status status);

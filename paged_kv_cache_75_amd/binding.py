@@ -70,9 +70,12 @@ def lib():
     c_int = ctypes.c_int
     signatures = {
         "pa_write_kv": ([vp, vp, vp, i32, vp, vp, desc, vp], c_int),
-        "pa_decode_workspace_bytes": ([i32, i32, desc, i32, i32], sz),
+        "pa_decode_workspace_bytes": ([i32, i32, desc, i32], sz),
+        "pa_decode_partitioned_workspace_bytes": ([i32, i32, desc, i32, i32], sz),
         "pa_decode": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
-                       vp, vp, sz, i32, vp], c_int),
+                       vp, vp, sz, vp], c_int),
+        "pa_decode_partitioned": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                                   vp, vp, sz, i32, vp], c_int),
         "pa_decode_sliding": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
                                i32, vp, vp, sz, i32, vp], c_int),
         "pa_append_decode": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
@@ -86,6 +89,7 @@ def lib():
         "pa_append_decode_fp8": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
                                   ctypes.c_float, ctypes.c_float, ctypes.c_float, vp, vp, sz, vp],
                                  c_int),
+        "pa_stream_read": ([vp, sz, vp, vp], c_int),
         "pa_profile_start": ([], c_int),
         "pa_profile_stop": ([ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)],
                             c_int),
@@ -118,6 +122,19 @@ def lib():
 
 def pa_status_string(status: int) -> str:
     return lib().pa_status_string(int(status)).decode()
+
+
+def pa_stream_read(buf, sink, stream=None) -> None:
+    """Read every byte of the device tensor ``buf`` once (the read-ceiling
+    measurement); ``sink`` is a device int32/uint32 tensor of at least one
+    element."""
+    _check(buf, "buf")
+    _check(sink, "sink", device=buf.device)
+    nbytes = buf.numel() * buf.element_size()
+    st = lib().pa_stream_read(buf.data_ptr(), nbytes - nbytes % 16, sink.data_ptr(),
+                              _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_stream_read")
 
 
 def pa_profile_start() -> None:
@@ -249,7 +266,7 @@ def pa_write_kv_fp8(k, v, slot_mapping, k_pool, v_pool, k_scale, v_scale, stream
 
 
 def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale, v_scale,
-                  out=None, max_context_len=None, workspace=None, stream=None):
+                  out=None, *, max_context_len, workspace=None, stream=None):
     """pa_decode over FP8 (E4M3) pools with per-pool scales."""
     torch = _torch()
     _on_current_device(k_pool, "k_pool")
@@ -267,12 +284,10 @@ def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale,
         raise ValueError("q head_dim differs from the pool's")
     if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
         raise ValueError("block_tables / context_lens rows must equal num_seqs")
-    if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if n else 0
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", dtype=q.dtype, device=dev)
-    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, 0)
+    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", device=dev)
@@ -288,7 +303,7 @@ def pa_decode_fp8(q, k_pool, v_pool, block_tables, context_lens, scale, k_scale,
 
 
 def pa_append_decode_fp8(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,
-                         k_scale, v_scale, out=None, max_context_len=None, workspace=None,
+                         k_scale, v_scale, out=None, *, max_context_len, workspace=None,
                          stream=None):
     """Quantize token T_i - 1 of every sequence (rows of new_k / new_v,
     [N][Hkv][D], q's dtype) into the FP8 pools and decode, in one call; same
@@ -314,12 +329,10 @@ def pa_append_decode_fp8(q, new_k, new_v, k_pool, v_pool, block_tables, context_
         _check(t, name, dtype=q.dtype, device=dev)
         if tuple(t.shape) != want:
             raise ValueError(f"{name} must be {want}")
-    if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if n else 0
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", dtype=q.dtype, device=dev)
-    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, 0)
+    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", device=dev)
@@ -336,27 +349,44 @@ def pa_append_decode_fp8(q, new_k, new_v, k_pool, v_pool, block_tables, context_
 
 
 def pa_decode_workspace_bytes(num_seqs: int, num_q_heads: int, desc: pa_pool_desc,
-                              max_context_len: int, partition_tokens: int = 0) -> int:
+                              max_context_len: int) -> int:
     return int(lib().pa_decode_workspace_bytes(int(num_seqs), int(num_q_heads),
-                                               ctypes.byref(desc), int(max_context_len),
-                                               int(partition_tokens)))
+                                               ctypes.byref(desc), int(max_context_len)))
 
 
-def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None,
-              max_context_len=None, workspace=None, partition_tokens: int = 0,
-              stream=None):
+def pa_decode_partitioned_workspace_bytes(num_seqs: int, num_q_heads: int, desc: pa_pool_desc,
+                                          max_context_len: int, partition_tokens: int) -> int:
+    return int(lib().pa_decode_partitioned_workspace_bytes(
+        int(num_seqs), int(num_q_heads), ctypes.byref(desc), int(max_context_len),
+        int(partition_tokens)))
+
+
+def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
+              max_context_len, workspace=None, stream=None):
     """Paged decode attention; returns ``out`` ([N][Hq][D], pool dtype).
 
-    ``max_context_len`` is the host bound on context_lens; when omitted it is
-    read from the device (a synchronizing copy).  ``workspace`` is a uint8 or
-    float32 device tensor of at least pa_decode_workspace_bytes(...) bytes;
-    when omitted a fresh one is taken from torch's caching allocator."""
+    ``max_context_len`` is the host bound on context_lens (the library never
+    reads device arrays on the host, so it is not derived here).
+    ``workspace`` is a uint8 or float32 device tensor of at least
+    pa_decode_workspace_bytes(...) bytes; when omitted a fresh one is taken
+    from torch's caching allocator."""
     return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
-                   max_context_len, workspace, partition_tokens, stream)
+                   max_context_len, workspace, 0, stream)
+
+
+def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, scale,
+                          partition_tokens: int, out=None, *, max_context_len, workspace=None,
+                          stream=None):
+    """pa_decode with fixed context partitions of ``partition_tokens`` tokens
+    (a multiple of 16) merged by the log-sum-exp reduce kernel."""
+    if int(partition_tokens) <= 0:
+        raise ValueError("partition_tokens must be positive (pa_decode is the library's split)")
+    return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
+                   max_context_len, workspace, int(partition_tokens), stream)
 
 
 def pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, window: int,
-                      out=None, max_context_len=None, workspace=None, partition_tokens: int = 0,
+                      out=None, *, max_context_len, workspace=None, partition_tokens: int = 0,
                       stream=None):
     """pa_decode over each sequence's last ``window`` tokens only (a layer
     trained with sliding-window attention)."""
@@ -364,12 +394,12 @@ def pa_decode_sliding(q, k_pool, v_pool, block_tables, context_lens, scale, wind
                    max_context_len, workspace, partition_tokens, stream, window=int(window))
 
 
-def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None,
-               max_context_len=None, max_query_len=None, stream=None):
+def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale, out=None, *,
+               max_context_len, max_query_len, stream=None):
     """Causal attention of each sequence's last M_i tokens (a prompt chunk or
     a decode token): q and out are [query_start[-1]][Hq][D]; rows
-    query_start[i] .. query_start[i+1]-1 belong to sequence i.  The host
-    bounds are read from the device when omitted (a synchronizing copy)."""
+    query_start[i] .. query_start[i+1]-1 belong to sequence i.
+    ``max_context_len`` and ``max_query_len`` are host bounds on T_i and M_i."""
     torch = _torch()
     _on_current_device(k_pool, "k_pool")
     desc = pool_desc(k_pool)
@@ -388,10 +418,6 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
         raise ValueError("q head_dim differs from the pool's")
     if int(block_tables.shape[0]) != n or int(query_start.shape[0]) != n + 1:
         raise ValueError("block_tables rows must equal num_seqs, query_start num_seqs + 1")
-    if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if n else 0
-    if max_query_len is None:
-        max_query_len = int((query_start[1:] - query_start[:-1]).max().item()) if n else 0
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", dtype=q.dtype, device=dev)
@@ -408,7 +434,7 @@ def pa_prefill(q, k_pool, v_pool, block_tables, context_lens, query_start, scale
 
 
 def pa_append_decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale,
-                     out=None, max_context_len=None, workspace=None,
+                     out=None, *, max_context_len, workspace=None,
                      partition_tokens: int = 0, stream=None):
     """Write token T_i - 1 of every sequence (rows of new_k / new_v,
     [N][Hkv][D]) into the pools through the block tables and decode, in one
@@ -435,8 +461,6 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
         raise ValueError("q head_dim differs from the pool's")
     if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
         raise ValueError("block_tables / context_lens rows must equal num_seqs")
-    if max_context_len is None:
-        max_context_len = int(context_lens.max().item()) if n else 0
     if out is None:
         out = torch.empty_like(q)
     _check(out, "out", dtype=q.dtype, device=dev)
@@ -448,7 +472,7 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
             _check(t, name, dtype=k_pool.dtype, device=dev)
             if tuple(t.shape) != want:
                 raise ValueError(f"{name} must be {want}")
-    need = pa_decode_workspace_bytes(n, hq, desc, max_context_len, partition_tokens)
+    need = pa_decode_partitioned_workspace_bytes(n, hq, desc, max_context_len, partition_tokens)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _check(workspace, "workspace", device=dev)
@@ -461,9 +485,14 @@ def _decode(q, new_k, new_v, k_pool, v_pool, block_tables, context_lens, scale, 
         st = lib().pa_decode_sliding(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
                                      *tail[:8], int(window), *tail[8:])
         where = "pa_decode_sliding"
-    elif new_k is None:
-        st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), *tail)
+    elif new_k is None and partition_tokens == 0:
+        st = lib().pa_decode(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                             *tail[:11], tail[12])
         where = "pa_decode"
+    elif new_k is None:
+        st = lib().pa_decode_partitioned(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                         *tail)
+        where = "pa_decode_partitioned"
     else:
         st = lib().pa_append_decode(q.data_ptr(), new_k.data_ptr(), new_v.data_ptr(),
                                     k_pool.data_ptr(), v_pool.data_ptr(), *tail)

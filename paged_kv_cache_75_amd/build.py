@@ -26,7 +26,7 @@ LIB_PATH = os.path.join(LIB_DIR, "libpa.so")
 ARCH = "gfx950"
 
 SOURCES = ["pa_plan.cpp", "pa_api.cpp", "pa_block_manager.cpp", "pa_sha256.cpp", "pa_kernels.hip",
-           "pa_copy.hip", "pa_check.hip", "pa_prefill.hip"]
+           "pa_copy.hip", "pa_check.hip", "pa_prefill.hip", "pa_measure.hip"]
 
 COMMON_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

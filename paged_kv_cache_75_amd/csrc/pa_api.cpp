@@ -107,14 +107,19 @@ pa_status pa_check_inputs(const int32_t* slot_mapping, int32_t num_tokens,
                                                                              : PA_ERR_HIP;
 }
 
-size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
-                                 const pa_pool_desc* pool, int32_t max_context_len,
-                                 int32_t partition_tokens) {
+size_t pa_decode_partitioned_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                             const pa_pool_desc* pool, int32_t max_context_len,
+                                             int32_t partition_tokens) {
   pa::DecodePlan plan;
   if (pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len, -1, partition_tokens,
                       &plan) != PA_OK)
     return 0;
   return plan.ws_bytes;
+}
+
+size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
+                                 const pa_pool_desc* pool, int32_t max_context_len) {
+  return pa_decode_partitioned_workspace_bytes(num_seqs, num_q_heads, pool, max_context_len, 0);
 }
 
 }  // extern "C"
@@ -195,7 +200,19 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     int32_t max_blocks_per_seq, const int32_t* context_lens,
                     int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
                     float scale, void* out, void* workspace, size_t workspace_bytes,
-                    int32_t partition_tokens, void* stream) {
+                    void* stream) {
+  return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
+                workspace_bytes, 0, 0, stream);
+}
+
+pa_status pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
+                                const pa_pool_desc* pool, const int32_t* block_tables,
+                                int32_t max_blocks_per_seq, const int32_t* context_lens,
+                                int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                                float scale, void* out, void* workspace, size_t workspace_bytes,
+                                int32_t partition_tokens, void* stream) {
+  if (partition_tokens <= 0) return PA_ERR_INVALID_ARGUMENT;
   return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
                 context_lens, num_seqs, max_context_len, num_q_heads, scale, out, workspace,
                 workspace_bytes, partition_tokens, 0, stream);
@@ -314,6 +331,17 @@ pa_status pa_prefill(const void* q, const void* k_pool, const void* v_pool,
   const hipError_t e = pa::launch_prefill(a, pool->dtype, pool->head_dim, group,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;
+}
+
+pa_status pa_stream_read(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+  if (bytes == 0) return PA_OK;
+  if (!buf || !sink || bytes % 16 != 0 || reinterpret_cast<uintptr_t>(buf) % 16 != 0)
+    return PA_ERR_INVALID_ARGUMENT;
+  if (bytes > (size_t(1) << 40)) return PA_ERR_UNSUPPORTED;
+  return pa::launch_stream_read(buf, static_cast<int64_t>(bytes), sink,
+                                static_cast<hipStream_t>(stream)) == hipSuccess
+             ? PA_OK
+             : PA_ERR_HIP;
 }
 
 pa_status pa_profile_start(void) {

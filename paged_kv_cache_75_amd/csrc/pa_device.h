@@ -163,6 +163,44 @@ __device__ inline float row_sum16(float x) {
   return x;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave on the vector ALU (DPP):
+// shifts by 1, 2, 4 and 8 within each 16-lane row (lanes shifted in from
+// outside the row add 0), then row 0's total into row 1 and row 2's total into
+// row 3 (lane 15's and lane 47's values, broadcast), then lane 31's total into
+// rows 2 and 3.
+__device__ __forceinline__ int wave_scan_incl(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15, rows 1 and 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31, rows 2 and 3
+  return x;
+}
+// the value of the last lane (the total after wave_scan_incl)
+__device__ __forceinline__ int wave_last(int x) { return __builtin_amdgcn_readlane(x, kWave - 1); }
+
+// The maximum (sum) over the four lanes c, c + 16, c + 32, c + 48 of a column:
+// row swaps on the vector ALU rather than permutes through LDS.  The sum adds
+// the pairs (rows 0 + 1) and (rows 2 + 3) first, in the same order on every
+// lane.
+__device__ __forceinline__ float column_max(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
+}
+__device__ __forceinline__ float column_sum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 __device__ inline void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

@@ -117,6 +117,10 @@ hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const DecodeArgs& a, int32_t dtype, int32_t head_dim, int32_t group,
                           hipStream_t stream);
 
+// Streaming read of `bytes` (a multiple of 16) at `buf` (16-byte aligned);
+// writes sink[0] only for data crafted to match a constant (measurement only).
+hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hipStream_t stream);
+
 // Kernel timing (measurement only): start attaching events to the attention
 // kernel of each decode call; stop, wait for those events and report.
 void profile_start();

@@ -247,6 +247,15 @@ template <int DT> __device__ inline uint4 fp8x8_to(const uint4& c, int h) {
                     fp8x2_to<DT>(w1 >> 16));
 }
 
+// the float32 value of a 16-bit element held in a short
+template <int DT> __device__ inline float elem_value(short h);
+template <> __device__ inline float elem_value<PA_BF16>(short h) {
+  return __uint_as_float(uint32_t(static_cast<uint16_t>(h)) << 16);
+}
+template <> __device__ inline float elem_value<PA_F16>(short h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
 template <int DT, int D, int G>
 struct MfmaPv {
   using GE = Geo<DT, D, G>;
@@ -337,8 +346,7 @@ struct MfmaPv {
       s[i] = row >= first && row < live ? sc[i] * a.scale_log2 : -INFINITY;
       mx = fmaxf(mx, s[i]);
     }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+    mx = column_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float m_use = m_new == -INFINITY ? 0.0f : m_new;
     alpha_ = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -352,11 +360,19 @@ struct MfmaPv {
     m_run = m_new;
   }
 
-  // phase 3: O^T = alpha O^T + V^T . P^T
+  // phase 3: O^T = alpha O^T + V^T . P^T.  P enters the matrix cores as two
+  // element-type operands, hi = P rounded and lo = (P - hi) rounded, so the
+  // products carry P to about twice the element type's precision (P rounded
+  // once would cost up to half an ulp of the element type per weight; the
+  // sum l is taken on the float32 P)
   __device__ __forceinline__ void accumulate(const char* vt) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) o[n] *= alpha_;
     const v4i16 pb = pack4<DT>(p_);
+    float rest[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) rest[i] = p_[i] - elem_value<DT>(pb[i]);
+    const v4i16 pl = pack4<DT>(rest);
     wave_sync_lds();
     // A operand of tile n: lane (gq, r) points at V[4gq + r/4][16n + 4(r%4)]
     const int row = 4 * gq + (c >> 2);
@@ -368,34 +384,66 @@ struct MfmaPv {
       const v4i16 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
           (lds_v4i16*)(rbase + ((chunk ^ sw) << 4)));
       o[n] = mfma_pv<DT>(av, pb, o[n]);
+      o[n] = mfma_pv<DT>(av, pl, o[n]);
     }
     wave_sync_lds();
   }
 
-  // One wave holds the whole segment: write its result from registers.
-  // complete: out rows (row0 + c) get O/l; otherwise the piece slot gets
-  // O/l, the running max and the sum.  Lane (gq, c < G) owns d = 16n+4gq+i.
-  // out_scale multiplies the result (the value scale of FP8 pools; 1 otherwise)
-  __device__ __forceinline__ void store_result(const DecodeArgs& a, int64_t row0, bool complete,
-                                               int piece, float out_scale = 1.0f) {
-    float l = l_run;
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+  // the sum of a head's weights (its four lanes), on every lane
+  __device__ __forceinline__ float head_sum() const { return column_sum(l_run); }
+
+  // Compact copy of a piece (O / l times out_scale, and the max and sum per
+  // head) for storing later.  Only the first G of the 16 head columns hold
+  // results, so the copy spreads them over the other columns' lanes: lane
+  // (gq, c) keeps head c % kStashHeads, output tiles b * kStashN + j
+  // (j < kStashN) with b = c / kStashHeads, and the max and sum of its head.
+  static constexpr int kStashF = G <= 4 ? 4 : G <= 8 ? 2 : 1;
+  static constexpr int kStashHeads = 16 / kStashF;
+  static constexpr int kStashN = NT / kStashF;
+  __device__ __forceinline__ void stash(f32x4* dst, float& m_out, float& l_out, float out_scale) {
+    const float l = head_sum();
+    const float inv = (1.0f / l) * out_scale;
+    const int b = c / kStashHeads;
+    const int src = (gq << 4) | (c % kStashHeads);
+#pragma unroll
+    for (int j = 0; j < kStashN; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float v = 0.0f;
+#pragma unroll
+        for (int b2 = 0; b2 < kStashF; ++b2) {
+          const float t = __shfl(o[b2 * kStashN + j][i] * inv, src, kWave);
+          v = b == b2 ? t : v;
+        }
+        dst[j][i] = v;
+      }
+    m_out = __shfl(m_run, src, kWave);
+    l_out = __shfl(l, src, kWave);
+  }
+  // store a compact copy to piece slot `piece` of the workspace
+  __device__ __forceinline__ void store_stash(const DecodeArgs& a, int piece, const f32x4* st,
+                                              float m, float l) {
+    const int head = c % kStashHeads;
+    if (head >= G) return;
+    const int b = c / kStashHeads;
+    float* po = a.ws_o + (int64_t(piece) * G + head) * D;
+#pragma unroll
+    for (int j = 0; j < kStashN; ++j)
+      *reinterpret_cast<f32x4*>(po + 16 * (b * kStashN + j) + 4 * gq) = st[j];
+    if (gq == 0 && b == 0) {
+      a.ws_ml[(piece * G + head) * 2] = m;
+      a.ws_ml[(piece * G + head) * 2 + 1] = l;
+    }
+  }
+
+  // O / l times out_scale, rounded to the element type, into a [G][D] LDS
+  // copy of the group's output rows (lane (gq, c < G): d = 16n + 4gq + i)
+  __device__ __forceinline__ void stage_output(char* dst, float out_scale) {
+    const float l = head_sum();
     if (c >= G) return;
     const float inv = (1.0f / l) * out_scale;
-    if (complete) {
 #pragma unroll
-      for (int n = 0; n < NT; ++n) store4<DT>(a.out, (row0 + c) * D + 16 * n + 4 * gq, o[n] * inv);
-    } else {
-      float* po = a.ws_o + (int64_t(piece) * G + c) * D;
-#pragma unroll
-      for (int n = 0; n < NT; ++n)
-        *reinterpret_cast<f32x4*>(po + 16 * n + 4 * gq) = o[n] * inv;
-      if (gq == 0) {
-        a.ws_ml[(piece * G + c) * 2] = m_run;
-        a.ws_ml[(piece * G + c) * 2 + 1] = l;
-      }
-    }
+    for (int n = 0; n < NT; ++n) store4<DT>(dst, c * D + 16 * n + 4 * gq, o[n] * inv);
   }
 
   // wave totals into sm: O^T lane (gq, c), element i of tile n = head c, d = 16n + 4gq + i
@@ -734,51 +782,91 @@ __device__ inline void zero_rows(const DecodeArgs& a, int64_t row0, int nrows) {
 // Balanced split (the default for 16-bit elements and blocks of >= 16
 // tokens).  The grid holds as many one-wave workgroups as the GPU keeps
 // resident.  The flattened work (sequence, kv head, 16-token tile) is cut
-// into equal contiguous shares, one per wave, so long and short sequences
-// load every wave alike.
+// into contiguous shares, one per wave, sized so that long and short
+// sequences load every wave alike.
 //
-// A wave lists the (sequence, kv head) segments of its share (up to kSegCap
-// at a time), copies their query rows to LDS and computes, 64 tiles per
-// register batch, each tile's byte offset in the pools and its number of live
-// rows.  It then streams the tiles without draining at segment boundaries:
-// keys are requested two tiles ahead, values one tile ahead.  A segment that
-// covers its whole pair is written to the output directly; a pair cut by a
-// share boundary leaves a "piece" (max, sum, normalised output per head) in
-// slot 0 (the share's first segment) or slot 1 (its last); the first piece
-// also records how many shares the pair spans, and the piece merge kernel
-// combines them.
+// Start of a wave: one round trip brings every length (lane l holds
+// sequences l, l + 64, ...); a scan over them gives each sequence's place in
+// the flattened work, and the share's segments ((sequence, kv head) pairs or
+// parts of them) are found by the lanes in parallel, one candidate sequence
+// per lane.  A second round trip brings the block-table entries of the first
+// 64 tiles and the segments' query rows, and the first tiles' keys and values
+// are requested.  Tiles then stream without draining at segment boundaries:
+// keys two tiles ahead, values one tile ahead, the table entries of the next
+// 64 tiles half a batch ahead.
+//
+// Nothing is stored while tiles are in flight (a store counts in the same
+// in-order counter as the loads, so every later wait would include it): a
+// complete pair's output is staged in LDS over its query rows, the share's
+// first segment, when it is a piece of a pair cut by the share's start, is
+// kept in registers, and all of it is written after the run's last tile.  A
+// pair cut by a share boundary leaves a "piece" (max, sum, normalised output
+// per head) in slot 0 (the share's first segment) or slot 1 (its last); the
+// first piece also records how many shares the pair spans, and the piece
+// merge kernel combines them.
 // ---------------------------------------------------------------------------
 constexpr int kPieceFirst = 1;   // the piece starts at the pair's first tile
 constexpr int kPieceLast = 2;    // the piece ends at the pair's last tile
 constexpr int kHdrInts = 8;      // valid, seq, kv head, flags, pieces, (pad)
-constexpr int kQStageBytes = 8192;
+constexpr int kQStageBytes = 6144;   // LDS for query rows (and new rows) of one run
 constexpr int kMetaLive = 0x1f;    // tile descriptor: live rows (1..16)
 constexpr int kMetaAppend = 0x20;  // tile descriptor: the last live row is appended
 constexpr int kMetaStore = 0x40;   // ... and its table entry lies in the pool
 
 constexpr int kPairCost = 1;
 
+// Share sizes by the parity of the workgroup index.  Workgroup i runs on XCD
+// i mod 8, and on MI355X the odd XCD of each even/odd pair streams these
+// reads about 6% slower (per-XCD wave end times over full-size batches:
+// odd/even 1.04-1.08, whichever shares the XCDs are given), so odd shares
+// are made that much smaller.  The split stays a fixed function of the
+// lengths, so results do not depend on timing.
+constexpr int kEvenWeight = 33;
+constexpr int kOddWeight = 31;
+
 __device__ inline int pair_units(int T, int window) {
   const int tiles = attended_tiles(T, window);
   return tiles ? tiles + kPairCost : 0;
 }
 
+__device__ inline long long share_weight(int w) {
+  return static_cast<long long>(w >> 1) * (kEvenWeight + kOddWeight) + ((w & 1) ? kEvenWeight : 0);
+}
+// first unit of share w of nsh (total units < 2^31)
+__device__ inline int share_lo(int total, int w, int nsh) {
+  return static_cast<int>(static_cast<long long>(total) * share_weight(w) / share_weight(nsh));
+}
+// the share holding unit u < total
+__device__ inline int share_of(int total, int u, int nsh) {
+  int w = static_cast<int>(static_cast<long long>(u) * nsh / total);
+  w = min(w, nsh - 1);
+  while (w + 1 < nsh && share_lo(total, w + 1, nsh) <= u) ++w;
+  while (w > 0 && share_lo(total, w, nsh) > u) --w;
+  return w;
+}
+
 template <int DT, int D, int G, bool kAppend>
 struct StreamSmem {
+  static constexpr int kRowBytes = Geo<DT, D, G>::kRowBytes;
   static constexpr int kQBytes = G * D * 2;
   // appending decode: each segment's new K and V rows sit beside its queries
-  static constexpr int kNewBytes = kAppend ? 2 * Geo<DT, D, G>::kRowBytes : 0;
-  static constexpr int kSegCap = std::max(2, std::min(16, kQStageBytes / (kQBytes + kNewBytes)));
+  static constexpr int kNewBytes = kAppend ? 2 * kRowBytes : 0;
+  static constexpr int kSegCap = std::max(1, std::min(16, kQStageBytes / (kQBytes + kNewBytes)));
   alignas(16) char vtile[MfmaPv<DT, D, G>::kScratchBytes];
+  // a segment's query rows; a complete pair's output rows once it is done
   alignas(16) char q[kSegCap][kQBytes];
-  int32_t len[kMaxSplitSeqs];
+  // per sequence: pair units before it (per kv head) and its clamped length
+  int2 seq[kMaxSplitSeqs + 1];
   int32_t seg_seq[kSegCap];
   int32_t seg_g[kSegCap];
-  int32_t seg_tile0[kSegCap];
-  int32_t seg_start[kSegCap];
+  int32_t seg_tile0[kSegCap];     // absolute tile index of the segment's first tile
+  int32_t seg_start[kSegCap];     // its index in the run's tile list
   int32_t seg_n[kSegCap];
-  int32_t seg_flags[kSegCap];
-  int32_t seg_pieces[kSegCap];
+  int32_t seg_T[kSegCap];
+  int32_t seg_flags[kSegCap];     // kPieceFirst | kPieceLast, 4: the share's first segment
+  int32_t seg_pieces[kSegCap];    // shares the pair spans (pieces that start it)
+  int32_t run_end;                // unit after the run's last segment
+  int32_t run_seq;                // sequence of the run's last segment
   alignas(16) char newkv[kAppend ? kSegCap : 1][kAppend ? kNewBytes : 16];
   int64_t new_dst[kAppend ? kSegCap : 1];   // pool byte offset of the new row, or -1
 };
@@ -787,6 +875,7 @@ template <int DT, int D, int G, bool kAppend, bool kWindow, bool kFp8>
 __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   using GE = Geo<DT, D, G>;
   using SM = StreamSmem<DT, D, G, kAppend>;
+  using TM = MfmaPv<DT, D, G>;
   const int window = kWindow ? a.window : 0;      // 0: every token
   // pool rows: D codes (FP8 pools) or D elements of DT; the query rows, the LDS
   // value tile and the tile math always use DT
@@ -796,6 +885,8 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   constexpr int RPI = kWave / CPR;                // value rows per load instruction
   constexpr int VS = kTileTokens / RPI;           // value loads per lane per tile
   constexpr int kRowBytes = GE::kRowBytes;
+  constexpr int kRows = kMaxSplitSeqs / kWave;
+  constexpr int kQChunks = SM::kQBytes / 16;
   __shared__ SM sm;
 
   const int w = blockIdx.x;
@@ -804,189 +895,209 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   const int Hkv = a.num_kv_heads;
   const int Hq = a.num_q_heads;
   const int lane = threadIdx.x;
+  const int nrows = (N + kWave - 1) / kWave;
 
-  if (lane < 2) a.ws_hdr[(2 * w + lane) * kHdrInts] = 0;   // both piece slots empty so far
-
-  // clamped lengths into LDS; tiles of this lane's run of sequences; prefix
-  const int chunk = (N + kWave - 1) / kWave;
-  const int i0 = min(N, lane * chunk);
-  const int i1 = min(N, i0 + chunk);
-  // Work is measured in units: a (sequence, kv head) pair of n tiles costs
-  // n + kPairCost units, the extra ones standing for the fixed cost of a
-  // segment (query rows, the partial last tile, the result store).
-  long long mine = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int T = min(max(a.context_lens[i], 0), a.max_context_len);
-    sm.len[i] = T;
-    mine += pair_units(T, window);
-  }
-  long long incl = mine;
+  // ---- clamped lengths: every load in flight at once (lanes past the last
+  //      sequence repeat its load and count nothing) ----
+  int len[kRows];
 #pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const long long y = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += y;
+  for (int r = 0; r < kRows; ++r) len[r] = a.context_lens[min(r * kWave + lane, N - 1)];
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+    len[r] = r * kWave + lane < N ? min(max(len[r], 0), a.max_context_len) : 0;
+  // ---- pair units before each sequence: a scan over the lanes, row by row ----
+  int pre[kRows];
+  int carry = 0;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r) {
+    pre[r] = 0;
+    if (r < nrows) {
+      const int u = pair_units(len[r], window);
+      const int incl = wave_scan_incl(u);
+      pre[r] = carry + incl - u;
+      const int s = r * kWave + lane;
+      if (s < N) sm.seq[s] = make_int2(pre[r], len[r]);
+      carry += wave_last(incl);
+    }
   }
-  const long long all_units = __shfl(incl, kWave - 1, kWave);
-  const long long excl = incl - mine;
+  if (lane == 0) sm.seq[N] = make_int2(carry, 0);
+  // units: per (sequence, kv head) pair, its tiles plus kPairCost (the fixed
+  // cost of a segment: query rows, the partial last tile, the result)
+  const int total = Hkv * carry;                  // below 2^31 (the plan checks it)
+  const int want = (total + a.min_split_tiles - 1) / a.min_split_tiles;
+  const int nsh = max(1, min(W, want));
+  const int lo = (w < nsh && total > 0) ? share_lo(total, w, nsh) : 0;
+  const int hi = (w < nsh && total > 0) ? share_lo(total, w + 1, nsh) : 0;
+  // the share's first sequence: the last s whose work starts at or before lo
+  int first_seq = -1;
+#pragma unroll
+  for (int r = 0; r < kRows; ++r)
+    if (r < nrows)
+      first_seq += __popcll(__ballot(r * kWave + lane < N && Hkv * pre[r] <= lo));
   wave_sync_lds();
 
-  const int lb = a.log2_block;
-  const int bmask = (1 << lb) - 1;
-
-  // zero-length sequences get zero rows (spread over every workgroup)
-  for (int s = w; s < N; s += W)
-    if (sm.len[s] == 0) zero_rows<DT, D>(a, int64_t(s) * Hq, Hq);
-
-  const long long total = all_units * Hkv;
-  const long long want = (total + a.min_split_tiles - 1) / a.min_split_tiles;
-  const long long Weff = max(1LL, min(static_cast<long long>(W), want));
-  if (w >= Weff) return;
-  const long long lo = total * w / Weff;
-  const long long hi = total * (w + 1) / Weff;
-  if (lo >= hi) return;
-  // the lane whose run of sequences holds tile lo
-  const bool holds = mine > 0 && lo >= excl * Hkv && lo < (excl + mine) * Hkv;
-  const unsigned long long holders = __ballot(holds);
-  if (holders == 0) return;          // unreachable for lo < total
-  const int first = __builtin_ctzll(holders);
-  int s = __builtin_amdgcn_readfirstlane(first * chunk);
-  long long cum = __shfl(excl, first, kWave);
-
-  MfmaPv<DT, D, G> tm;
+  TM tm;
   tm.set_lane(lane);
   const int gq = lane >> 4, c = lane & 15, rho = lane / CPR, chi = lane % CPR;
   const int k_off = c * kPoolRowBytes + gq * 16;      // key chunk gq of row c; +64 per kk
   const int v_off = rho * kPoolRowBytes + chi * 16;   // value chunk chi of row rho
+  const int lb = a.log2_block;
+  const int bmask = (1 << lb) - 1;
   const int64_t blk_rows = int64_t(Hkv) << lb;
   const char* kbase = static_cast<const char*>(a.k_pool);
   const char* vbase = static_cast<const char*>(a.v_pool);
+  const float out_scale = kFp8 ? a.v_scale : 1.0f;
 
-  long long pos = lo;
-  while (pos < hi && s < N) {
-    // ---- the next run of segments (uniform walk over LDS lengths) ----
-    int nseg = 0, ntot = 0;
-    while (pos < hi && s < N && nseg < SM::kSegCap) {
-      const int T = __builtin_amdgcn_readfirstlane(sm.len[s]);
-      const int units = pair_units(T, window);
-      const int tiles = units - (units ? kPairCost : 0);
-      const long long base = cum * Hkv;
-      if (pos >= base + static_cast<long long>(units) * Hkv) {
-        cum += units;
-        ++s;
-        continue;
+  // piece headers of the share (slot 0: its first segment, slot 1: its
+  // last), written when the share is done
+  // (valid, sequence, kv head, flags, pieces) of each slot
+  int h0_valid = 0, h0_seq = 0, h0_g = 0, h0_flags = 0, h0_pieces = 0;
+  int h1_valid = 0, h1_seq = 0, h1_g = 0, h1_flags = 0, h1_pieces = 0;
+  // the share's first segment when it is a piece and more segments follow:
+  // normalised output, max and sum, stored when the share is done
+  f32x4 stash_o[TM::kStashN];
+  float stash_m = 0.0f, stash_l = 0.0f;
+  bool stashed = false;
+
+  int pos = lo;
+  int s_cur = max(first_seq, 0);
+  while (pos < hi) {
+    // ---- the next run of segments: lane j looks at sequence s_cur + j ----
+    int nmine = 0, g_first = 0, P = 0, u = 0, T = 0, my_tiles = 0;
+    const int s_lane = s_cur + lane;
+    if (s_lane < N) {
+      const int2 cur = sm.seq[s_lane];
+      P = cur.x;
+      T = cur.y;
+      u = sm.seq[s_lane + 1].x - P;
+      const int beg = Hkv * P;
+      const int a0 = max(pos, beg), a1 = min(hi, beg + Hkv * u);
+      if (u > 0 && a0 < a1) {
+        g_first = (a0 - beg) / u;
+        int g_last = (a1 - 1 - beg) / u;
+        // a pair the share reaches only through its first unit holds none of its tiles
+        if (a1 - (beg + g_last * u) <= kPairCost) --g_last;
+        nmine = max(0, g_last - g_first + 1);
       }
-      // pos - base < Hkv * units, below 2^31 (the plan checks it)
-      const int r = int(pos - base);
-      const int g = r / units;
-      const long long pair_start = base + static_cast<long long>(g) * units;
-      const long long pair_end = pair_start + units;
-      const long long seg_end = min(hi, pair_end);
-      // the pair's first kPairCost units carry no tiles
-      const int tile0 = max(0, int(pos - pair_start) - kPairCost);
-      const int tile1 = int(seg_end - pair_start) - kPairCost;
-      if (tile1 <= tile0) {           // this share holds none of the pair's tiles
-        pos = seg_end;
-        continue;
+    }
+    int incl = nmine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += y;
+    }
+    const int seg_before = incl - nmine;
+    const int nseg_all = __shfl(incl, kWave - 1, kWave);
+    const int nseg = min(nseg_all, SM::kSegCap);
+    // tiles of this lane's segments that fit the run
+    const int beg = Hkv * P;
+    auto seg_tiles = [&](int i, int& t0, int& t1) {
+      const int ps = beg + (g_first + i) * u;
+      t0 = max(0, pos - ps - kPairCost);
+      t1 = min(hi, ps + u) - ps - kPairCost;
+    };
+    for (int i = 0; i < nmine && seg_before + i < SM::kSegCap; ++i) {
+      int t0, t1;
+      seg_tiles(i, t0, t1);
+      my_tiles += t1 - t0;
+    }
+    int tincl = my_tiles;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int y = __shfl_up(tincl, o, kWave);
+      if (lane >= o) tincl += y;
+    }
+    const int ntot = __shfl(tincl, kWave - 1, kWave);
+    {
+      int start = tincl - my_tiles;
+      const int wf = window_first(T, window) / kTileTokens;
+      for (int i = 0; i < nmine && seg_before + i < SM::kSegCap; ++i) {
+        const int slot = seg_before + i;
+        const int g = g_first + i;
+        int t0, t1;
+        seg_tiles(i, t0, t1);
+        const int ps = beg + g * u;
+        int flags = (t0 == 0 ? kPieceFirst : 0) | (t1 == u - kPairCost ? kPieceLast : 0);
+        if (slot == 0 && pos == lo) flags |= 4;
+        sm.seg_seq[slot] = s_lane;
+        sm.seg_g[slot] = g;
+        sm.seg_tile0[slot] = wf + t0;
+        sm.seg_start[slot] = start;
+        sm.seg_n[slot] = t1 - t0;
+        sm.seg_T[slot] = T;
+        sm.seg_flags[slot] = flags;
+        // a piece that starts its pair: shares up to the one holding its last unit
+        sm.seg_pieces[slot] = (flags & 3) == kPieceFirst ? share_of(total, ps + u - 1, nsh) - w + 1 : 1;
+        if constexpr (kAppend) sm.new_dst[slot] = -1;
+        if (slot == nseg - 1) {
+          sm.run_end = ps + kPairCost + t1;
+          sm.run_seq = s_lane;
+        }
+        start += t1 - t0;
       }
-      const int n = tile1 - tile0;
-      int flags = (tile0 == 0 ? kPieceFirst : 0) | (tile1 == tiles ? kPieceLast : 0);
-      // shares spanned by the pair: this one up to the one holding its last unit
-      const long long w_last = (pair_end * Weff - 1) / total;
-      if (lane == 0) {
-        sm.seg_seq[nseg] = s;
-        sm.seg_g[nseg] = g;
-        sm.seg_tile0[nseg] = window_first(T, window) / kTileTokens + tile0;   // absolute
-        sm.seg_start[nseg] = ntot;
-        sm.seg_n[nseg] = n;
-        sm.seg_flags[nseg] = flags | (pos == lo ? 0 : 4);
-        sm.seg_pieces[nseg] = int(w_last - w + 1);
-        if constexpr (kAppend) sm.new_dst[nseg] = -1;
-      }
-      ntot += n;
-      ++nseg;
-      pos = seg_end;
+    }
+    if (nseg == 0) {
+      // no tile of [pos, hi) among these 64 sequences (they are empty, or the
+      // share ends on a pair's tile-less first unit): move past them
+      const int s_next = s_cur + kWave;
+      if (s_next >= N) break;
+      pos = max(pos, Hkv * sm.seq[s_next].x);
+      s_cur = s_next;
+      continue;
     }
     wave_sync_lds();
-
-    // ---- query rows of these segments into LDS ----
-    constexpr int kQChunks = SM::kQBytes / 16;
-    for (int idx = lane; idx < nseg * kQChunks; idx += kWave) {
-      const int sg = idx / kQChunks;
-      const int part = idx - sg * kQChunks;
-      const uint4* src = reinterpret_cast<const uint4*>(
-          static_cast<const char*>(a.q) +
-          (int64_t(sm.seg_seq[sg]) * Hq + int64_t(sm.seg_g[sg]) * G) * kRowBytes);
-      *reinterpret_cast<uint4*>(sm.q[sg] + part * 16) = src[part];
-    }
-    if constexpr (kAppend && kFp8) {
-      // FP8 pools: each segment's new K and V rows are quantized here as the
-      // FP8 slot write does (the codes of x / scale) and kept as codes, which
-      // then take the pool rows' path through the tile math and are the bytes
-      // stored to the slot
-      constexpr int kQuadsPerRow = D / 4;                       // four codes per lane
-      for (int idx = lane; idx < nseg * 2 * kQuadsPerRow; idx += kWave) {
-        const int sg = idx / (2 * kQuadsPerRow);
-        const int part = idx - sg * 2 * kQuadsPerRow;
-        const bool is_v = part >= kQuadsPerRow;
-        const int quad = is_v ? part - kQuadsPerRow : part;
-        const uint2 x = *(reinterpret_cast<const uint2*>(
-                              static_cast<const char*>(is_v ? a.new_v : a.new_k) +
-                              (int64_t(sm.seg_seq[sg]) * Hkv + sm.seg_g[sg]) * kRowBytes) +
-                          quad);
-        const float sc = is_v ? a.v_scale : a.k_scale;
-        const uint32_t h[4] = {x.x & 0xffffu, x.x >> 16, x.y & 0xffffu, x.y >> 16};
-        const uint32_t word =
-            e4m3_codes4(half_bits_to_float<DT>(h[0]) / sc, half_bits_to_float<DT>(h[1]) / sc,
-                        half_bits_to_float<DT>(h[2]) / sc, half_bits_to_float<DT>(h[3]) / sc);
-        *reinterpret_cast<uint32_t*>(sm.newkv[sg] + (is_v ? kPoolRowBytes : 0) + 4 * quad) = word;
-      }
-    } else if constexpr (kAppend) {   // new K row, then new V row, of each segment's pair
-      for (int idx = lane; idx < nseg * 2 * CPR; idx += kWave) {
-        const int sg = idx / (2 * CPR);
-        const int part = idx - sg * 2 * CPR;
-        const bool is_v = part >= CPR;
-        const uint4* src = reinterpret_cast<const uint4*>(
-            static_cast<const char*>(is_v ? a.new_v : a.new_k) +
-            (int64_t(sm.seg_seq[sg]) * Hkv + sm.seg_g[sg]) * kRowBytes);
-        *reinterpret_cast<uint4*>(sm.newkv[sg] + part * 16) = src[is_v ? part - CPR : part];
-      }
-    }
+    const int run_end = nseg_all > nseg ? sm.run_end
+                                        : min(hi, s_cur + kWave < N ? Hkv * sm.seq[s_cur + kWave].x : hi);
+    const int run_seq = sm.run_seq;
+    const bool share_done = run_end >= hi;
 
     // ---- per-tile descriptors, 64 tiles per batch: lane j holds tile
     //      64*batch + j: its first row's byte offset and (segment, live rows)
-    int64_t doff = 0;
-    int dmeta = 0;
-    auto load_batch = [&](int batch) {
-      const int j = min(64 * batch + lane, ntot - 1);
+    auto tile_seg = [&](int j) {
       int sg = 0;
       for (int i = 1; i < nseg; ++i)
         if (j >= sm.seg_start[i]) sg = i;
-      const int seq = sm.seg_seq[sg];
-      const int t0 = (sm.seg_tile0[sg] + j - sm.seg_start[sg]) * kTileTokens;
-      const int T = sm.len[seq];
-      const int32_t* table = a.block_tables + int64_t(seq) * a.max_blocks_per_seq;
-      const int32_t entry = table[t0 >> lb];
+      return sg;
+    };
+    auto table_entry = [&](int j, int& sg, int& t0) {
+      sg = tile_seg(j);
+      t0 = (sm.seg_tile0[sg] + j - sm.seg_start[sg]) * kTileTokens;
+      const int32_t* table = a.block_tables + int64_t(sm.seg_seq[sg]) * a.max_blocks_per_seq;
+      return table[min(max(t0, 0) >> lb, a.max_blocks_per_seq - 1)];   // (always in range)
+    };
+    int64_t doff = 0;
+    int dmeta = 0;
+    auto make_desc = [&](int32_t entry, int sg, int t0) {
+      const int Ts = sm.seg_T[sg];
       const int64_t blk = min(max(entry, 0), a.num_blocks - 1);
       doff = (blk * blk_rows + (int64_t(sm.seg_g[sg]) << lb) + (t0 & bmask)) * kPoolRowBytes;
-      const int live = min(kTileTokens, T - t0);
+      const int live = min(kTileTokens, Ts - t0);
       // the sequence's newest token is in this tile and comes from new_k/new_v
-      const bool app = kAppend && t0 + live == T;
+      const bool app = kAppend && t0 + live == Ts;
       const bool in_pool = entry == blk;
-      const int first = kWindow ? max(0, window_first(T, window) - t0) : 0;   // rows before it
+      const int first = kWindow ? max(0, window_first(Ts, window) - t0) : 0;   // rows before it
       dmeta = live | (app ? kMetaAppend : 0) | (app && in_pool ? kMetaStore : 0) | (sg << 8) |
               (first << 12);
     };
+    int nx_entry = 0, nx_sg = 0, nx_t0 = 0;     // table entry of the next batch (prefetched)
+
     auto tile_off = [&](int k) -> int64_t {
       const uint32_t lo32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff), k & 63);
       const uint32_t hi32 = __builtin_amdgcn_readlane(static_cast<uint32_t>(doff >> 32), k & 63);
       return (int64_t(hi32) << 32) | lo32;
     };
     auto tile_meta = [&](int k) -> int { return __builtin_amdgcn_readlane(dmeta, k & 63); };
-    // a tile's rows are contiguous in one (block, kv head) run; the descriptor
-    // spans the live rows only, so rows past a sequence's end load as zeros
-    auto rsrc = [&](const char* base, int64_t off, int live) {
-      return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base + off), 0,
-                                               live * kPoolRowBytes, kBufferDword3);
+    // A tile's rows are contiguous in one (block, kv head) run.  The buffer
+    // descriptor starts at the first attended row (the window's first
+    // position in its tile, else row 0) and stops after the last row the
+    // pool supplies, so rows past a sequence's end, and rows before a
+    // window, read as zeros without touching memory: their lane offsets fall
+    // outside the descriptor (below its start they wrap around as unsigned
+    // offsets).
+    auto rsrc = [&](const char* base, int64_t off, int first, int rows) {
+      return __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<char*>(base + off + first * kPoolRowBytes), 0,
+          max(0, rows - first) * kPoolRowBytes, kBufferDword3);
     };
     struct Keys {
       KeyRegs<DT, D> r;
@@ -998,33 +1109,39 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
     auto pool_rows = [&](int meta) {
       return (meta & kMetaLive) - ((kAppend && (meta & kMetaAppend)) ? 1 : 0);
     };
+    auto first_row = [&](int meta) { return kWindow ? (meta >> 12) & 0xf : 0; };
     auto load_keys = [&](int k, Keys& kr) {
-      if ((k & 63) == 0 && k > 0) load_batch(k >> 6);
+      if ((k & 63) == 0 && k > 0) make_desc(nx_entry, nx_sg, nx_t0);
       const int meta = tile_meta(k);
       const int64_t off = tile_off(k);
-      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, off, pool_rows(meta));
+      const int first = first_row(meta);
+      const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, off, first, pool_rows(meta));
+      const int shift = first * kPoolRowBytes;
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         kr.r.k[kk] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk, 0, 0));
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk - shift, 0, 0));
       kr.meta = meta;
       kr.off = off;
     };
     ValRegs<DT, D> vr;
     auto load_vals = [&](int k) {
-      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_off(k), pool_rows(tile_meta(k)));
+      const int meta = tile_meta(k);
+      const int first = first_row(meta);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(vbase, tile_off(k), first, pool_rows(meta));
+      const int shift = first * kPoolRowBytes;
 #pragma unroll
       for (int s2 = 0; s2 < VS; ++s2)
-        vr.v[s2] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 rv, v_off + s2 * RPI * kPoolRowBytes, 0, 0));
+        vr.v[s2] = __builtin_bit_cast(
+            uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                       rv, v_off + s2 * RPI * kPoolRowBytes - shift, 0, 0));
     };
     // Appending tile: the newest row of the keys and of the values comes from
     // the segment's LDS copy of new_k / new_v (register selects only, so the
     // loads in flight are not waited for any earlier than the tile needs).
     // This wave, the only one to handle that row, also stores it to its pool
-    // slot once the run's tiles are done (a store in the tile pipeline would
-    // hold up the waits for the loads issued after it).  Nothing reads that
-    // slot in this launch: the descriptors of the tile stop short of it.
+    // slot once the run's tiles are done.  Nothing reads that slot in this
+    // launch: the descriptors of the tile stop short of it.
     auto put_new_row = [&](Keys& kr) {
       const int live = kr.meta & kMetaLive;
       const char* nk = sm.newkv[(kr.meta >> 8) & 0xf];
@@ -1042,13 +1159,91 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
         if (rho + s2 * RPI == live - 1) vr.v[s2] = y;
     };
 
-    load_batch(0);
-    wave_sync_lds();                 // the query rows are in LDS
+    // ---- second round trip: the first batch's table entries, then the
+    //      segments' query rows and new rows; the first tiles' keys and
+    //      values are requested before any of the rows is waited for ----
     Keys KA, KB;
-    load_keys(0, KA);
-    load_vals(0);
-    if (ntot > 1) load_keys(1, KB);
+    {
+      int sg0, t00;
+      const int32_t entry0 = table_entry(min(lane, ntot - 1), sg0, t00);
+      // (every lane loads: chunks past the run's last one repeat it, so the
+      // loads need no branches and stay in registers until written to LDS)
+      constexpr int kQPerLane = (SM::kSegCap * kQChunks + kWave - 1) / kWave;
+      uint4 qv[kQPerLane];
+#pragma unroll
+      for (int i = 0; i < kQPerLane; ++i) {
+        const int idx = min(lane + i * kWave, nseg * kQChunks - 1);
+        const int sgq = idx / kQChunks;
+        qv[i] = reinterpret_cast<const uint4*>(
+            static_cast<const char*>(a.q) +
+            (int64_t(sm.seg_seq[sgq]) * Hq + int64_t(sm.seg_g[sgq]) * G) *
+                kRowBytes)[idx - sgq * kQChunks];
+      }
+      // appending decode: each segment's new K row, then its new V row
+      // (16-bit elements: 2 * kRowBytes / 16 chunks per segment)
+      constexpr int kNewChunks = 2 * kRowBytes / 16;
+      constexpr int kNPerLane = kAppend ? (SM::kSegCap * kNewChunks + kWave - 1) / kWave : 1;
+      uint4 nv[kNPerLane];
+      if constexpr (kAppend) {
+#pragma unroll
+        for (int i = 0; i < kNPerLane; ++i) {
+          const int idx = min(lane + i * kWave, nseg * kNewChunks - 1);
+          const int sgn = idx / kNewChunks;
+          const int part = idx - sgn * kNewChunks;
+          const bool is_v = part >= kNewChunks / 2;
+          nv[i] = reinterpret_cast<const uint4*>(
+              static_cast<const char*>(is_v ? a.new_v : a.new_k) +
+              (int64_t(sm.seg_seq[sgn]) * Hkv + sm.seg_g[sgn]) *
+                  kRowBytes)[is_v ? part - kNewChunks / 2 : part];
+        }
+      }
+      make_desc(entry0, sg0, t00);
+      load_keys(0, KA);
+      load_vals(0);
+      if (ntot > 1) load_keys(1, KB);
+#pragma unroll
+      for (int i = 0; i < kQPerLane; ++i) {
+        const int idx = lane + i * kWave;
+        if (idx < nseg * kQChunks) {
+          const int sgq = idx / kQChunks;
+          *reinterpret_cast<uint4*>(sm.q[sgq] + (idx - sgq * kQChunks) * 16) = qv[i];
+        }
+      }
+      if constexpr (kAppend) {
+#pragma unroll
+        for (int i = 0; i < kNPerLane; ++i) {
+          const int idx = lane + i * kWave;
+          if (idx < nseg * kNewChunks) {
+            const int sgn = idx / kNewChunks;
+            const int part = idx - sgn * kNewChunks;
+            if constexpr (kFp8) {
+              // FP8 pools: the new rows are quantized as the FP8 slot write
+              // does (the codes of x / scale) and kept as codes, which then
+              // take the pool rows' path through the tile math and are the
+              // bytes stored to the slot: 8 elements -> 8 codes per chunk
+              const bool is_v = part >= kNewChunks / 2;
+              const int ch = is_v ? part - kNewChunks / 2 : part;
+              const float sc = is_v ? a.v_scale : a.k_scale;
+              const uint4 x = nv[i];
+              const uint32_t hw[8] = {x.x & 0xffffu, x.x >> 16, x.y & 0xffffu, x.y >> 16,
+                                      x.z & 0xffffu, x.z >> 16, x.w & 0xffffu, x.w >> 16};
+              float y[8];
+#pragma unroll
+              for (int e = 0; e < 8; ++e) y[e] = half_bits_to_float<DT>(hw[e]) / sc;
+              const uint2 codes = make_uint2(e4m3_codes4(y[0], y[1], y[2], y[3]),
+                                             e4m3_codes4(y[4], y[5], y[6], y[7]));
+              *reinterpret_cast<uint2*>(sm.newkv[sgn] + (is_v ? kPoolRowBytes : 0) + 8 * ch) =
+                  codes;
+            } else {
+              *reinterpret_cast<uint4*>(sm.newkv[sgn] + part * 16) = nv[i];
+            }
+          }
+        }
+      }
+    }
+    wave_sync_lds();                 // the query rows (and new rows) are in LDS
     int cur = -1;
+    int last_sg = -1;                // the run's last segment when it is a piece left in registers
     auto step = [&](int k, Keys& kr) {
       const int sg = (kr.meta >> 8) & 0xf;
       if (sg != cur) {               // a new segment begins
@@ -1059,10 +1254,12 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
         else
           tm.load_q_lds(sm.q[sg]);
       }
+      // the next batch's table entries, half a batch ahead
+      if ((k & 63) == 32 && (k | 63) + 1 < ntot)
+        nx_entry = table_entry(min((k | 63) + 1 + lane, ntot - 1), nx_sg, nx_t0);
       if constexpr (kAppend)
         if (kr.meta & kMetaAppend) put_new_row(kr);
-      const int first = kWindow ? (kr.meta >> 12) & 0xf : 0;
-      if (kWindow && first > 0) clear_rows_below(vr, first, rho);
+      const int first = first_row(kr.meta);
       if constexpr (kFp8) {
         // each chunk of 16 value codes becomes two 16-bit chunks of the row
 #pragma unroll
@@ -1071,7 +1268,7 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
           for (int h = 0; h < 2; ++h)
             *reinterpret_cast<uint4*>(sm.vtile + row * kRowBytes +
-                                      (((2 * chi + h) ^ MfmaPv<DT, D, G>::swz(row)) << 4)) =
+                                      (((2 * chi + h) ^ TM::swz(row)) << 4)) =
                 fp8x8_to<DT>(vr.v[s2], h);
         }
       } else {
@@ -1093,19 +1290,19 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       tm.accumulate(sm.vtile);
       if (k + 1 == sm.seg_start[sg] + sm.seg_n[sg]) {   // the segment's last tile
         const int flags = sm.seg_flags[sg];
-        const bool complete = (flags & 3) == (kPieceFirst | kPieceLast);
-        const int piece = 2 * w + ((flags & 4) ? 1 : 0);
-        const int seq = sm.seg_seq[sg];
-        const int g = sm.seg_g[sg];
-        tm.store_result(a, int64_t(seq) * Hq + int64_t(g) * G, complete, piece,
-                        kFp8 ? a.v_scale : 1.0f);
-        if (!complete && lane == 0) {
-          int32_t* hdr = a.ws_hdr + piece * kHdrInts;
-          hdr[1] = seq;
-          hdr[2] = g;
-          hdr[3] = flags & 3;
-          hdr[4] = sm.seg_pieces[sg];
-          hdr[0] = 1;
+        if ((flags & 3) == (kPieceFirst | kPieceLast)) {
+          tm.stage_output(sm.q[sg], out_scale);          // over its (spent) query rows
+        } else if ((flags & 4) && !(share_done && k + 1 == ntot)) {
+          // the share's first segment, a piece, with more segments to come
+          tm.stash(stash_o, stash_m, stash_l, out_scale);
+          stashed = true;
+          h0_valid = 1;
+          h0_seq = sm.seg_seq[sg];
+          h0_g = sm.seg_g[sg];
+          h0_flags = flags & 3;
+          h0_pieces = sm.seg_pieces[sg];
+        } else {
+          last_sg = sg;              // the share's last segment: stored after the loop
         }
       }
     };
@@ -1114,8 +1311,49 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       if (k + 1 >= ntot) break;
       step(k + 1, KB);
     }
+
+    // ---- the run is done: results and appended rows leave the wave ----
+    if (last_sg >= 0) {
+      const int flags = sm.seg_flags[last_sg];
+      const int slot = (flags & 4) ? 0 : 1;
+      const int piece = 2 * w + slot;
+      const float l = tm.head_sum();
+      if (c < G) {
+        const float inv = (1.0f / l) * out_scale;
+        float* po = a.ws_o + (int64_t(piece) * G + c) * D;
+#pragma unroll
+        for (int n = 0; n < TM::NT; ++n)
+          *reinterpret_cast<f32x4*>(po + 16 * n + 4 * gq) = tm.o[n] * inv;
+        if (gq == 0) {
+          a.ws_ml[(piece * G + c) * 2] = tm.m_run;
+          a.ws_ml[(piece * G + c) * 2 + 1] = l;
+        }
+      }
+      if (slot == 0) {
+        h0_valid = 1;
+        h0_seq = sm.seg_seq[last_sg];
+        h0_g = sm.seg_g[last_sg];
+        h0_flags = flags & 3;
+        h0_pieces = sm.seg_pieces[last_sg];
+      } else {
+        h1_valid = 1;
+        h1_seq = sm.seg_seq[last_sg];
+        h1_g = sm.seg_g[last_sg];
+        h1_flags = flags & 3;
+        h1_pieces = sm.seg_pieces[last_sg];
+      }
+    }
+    wave_sync_lds();                 // staged outputs and new_dst records
+    for (int idx = lane; idx < nseg * kQChunks; idx += kWave) {
+      const int sg = idx / kQChunks;
+      if ((sm.seg_flags[sg] & 3) != (kPieceFirst | kPieceLast)) continue;
+      const int part = idx - sg * kQChunks;
+      reinterpret_cast<uint4*>(static_cast<char*>(a.out) +
+                               (int64_t(sm.seg_seq[sg]) * Hq + int64_t(sm.seg_g[sg]) * G) *
+                                   kRowBytes)[part] =
+          *reinterpret_cast<const uint4*>(sm.q[sg] + part * 16);
+    }
     if constexpr (kAppend) {
-      wave_sync_lds();               // new_dst records of this run
       for (int sg = 0; sg < nseg; ++sg) {
         const int64_t dst = sm.new_dst[sg];
         if (dst >= 0 && lane < 2 * CPR) {
@@ -1127,7 +1365,23 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
       }
     }
     wave_sync_lds();                 // LDS records are rewritten by the next run
+    pos = run_end;
+    s_cur = nseg_all > nseg ? run_seq : min(N, s_cur + kWave);
   }
+
+  // ---- the share is done ----
+  if (stashed) tm.store_stash(a, 2 * w, stash_o, stash_m, stash_l);
+  if (lane < 2) {
+    int32_t* hdr = a.ws_hdr + (2 * w + lane) * kHdrInts;
+    hdr[0] = lane ? h1_valid : h0_valid;
+    hdr[1] = lane ? h1_seq : h0_seq;
+    hdr[2] = lane ? h1_g : h0_g;
+    hdr[3] = lane ? h1_flags : h0_flags;
+    hdr[4] = lane ? h1_pieces : h0_pieces;
+  }
+  // zero-length sequences get zero rows (spread over every workgroup)
+  for (int s = w; s < N; s += W)
+    if (sm.seq[s].y == 0) zero_rows<DT, D>(a, int64_t(s) * Hq, Hq);
 }
 
 // Combine the pieces of every pair that starts inside this share: the piece

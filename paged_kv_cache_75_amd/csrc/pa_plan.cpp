@@ -90,12 +90,13 @@ pa_status plan_decode(int32_t num_seqs, int32_t num_q_heads, const pa_pool_desc*
   const size_t D = size_t(pool->head_dim);
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };
   // balanced split: 16-bit elements (matrix-core P.V), blocks holding whole
-  // 16-token tiles, and a batch whose lengths fit the kernel's LDS copy
-  // (the kernel indexes one sequence's work, kv heads x (tiles + 1), in 32 bits)
-  const int64_t seq_units =
-      int64_t(pool->num_kv_heads) * (max_context_len / kTileTokens + 2);
+  // 16-token tiles, and a batch whose lengths fit the kernel's LDS copy (the
+  // kernel counts the whole batch's work, kv heads x (tiles + 1) per
+  // sequence, in 32 bits)
+  const int64_t batch_units = int64_t(num_seqs) * pool->num_kv_heads *
+                              (int64_t(max_context_len) / kTileTokens + 2);
   if (partition_tokens == 0 && num_seqs <= kMaxSplitSeqs && pool->dtype != PA_F32 &&
-      pool->block_size >= kTileTokens && seq_units < (int64_t{1} << 31)) {
+      pool->block_size >= kTileTokens && batch_units < (int64_t{1} << 31)) {
     // two piece slots per workgroup share; an 8-int header per piece
     const size_t pieces = size_t(kMaxSplits) * 2;
     p.balanced = true;

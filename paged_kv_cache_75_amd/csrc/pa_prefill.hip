@@ -76,17 +76,6 @@ __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int k, int& len)
   return s;
 }
 
-// The maximum over the four lanes of each column (lanes c, c + 16, c + 32,
-// c + 48): row swaps on the vector ALU rather than permutes through LDS.
-__device__ __forceinline__ float column_max(float x) {
-  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  x = fmaxf(__uint_as_float(p[0]), __uint_as_float(p[1]));
-  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return fmaxf(__uint_as_float(q[0]), __uint_as_float(q[1]));
-}
-
 // Softmax reference of the prefill: a column keeps its reference m until a
 // step's maximum exceeds it by more than kRefSlack (log2 units); only then are
 // the wave's sums and outputs rescaled (a wave-uniform branch).  The result is
@@ -94,6 +83,17 @@ __device__ __forceinline__ float column_max(float x) {
 // inside float32 and bfloat16 range, and the relative precision of the
 // weights does not depend on their scale.
 constexpr float kRefSlack = 8.0f;
+
+// x rounded to the nearest element value (ties to even), as a float; x is a
+// finite weight in [0, 1]
+template <int DT> __device__ inline float round_to_elem(float x);
+template <> __device__ inline float round_to_elem<PA_BF16>(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+}
+template <> __device__ inline float round_to_elem<PA_F16>(float x) {
+  return static_cast<float>(static_cast<_Float16>(x));
+}
 
 // One 16-column block of a prefill wave: Q^T operand, O^T accumulators, the
 // running reference and sum, and the step's weights.
@@ -169,6 +169,10 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
       t.m_run = m_new;
     }
   }
+  // The weights enter P.V rounded to the element type; the sum l adds the
+  // same rounded weights, so the result is an exact weighted average of the
+  // value rows with those weights (its error from the rounding then scales
+  // with how far the values lie from the result, not with their size).
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     PrefillCols<DT, D>& t = cols[b];
@@ -176,7 +180,7 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
     float psum = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      t.p[i] = __builtin_amdgcn_exp2f(s[b][i] - m_use);
+      t.p[i] = round_to_elem<DT>(__builtin_amdgcn_exp2f(s[b][i] - m_use));
       psum += t.p[i];
     }
     t.l_run += psum;

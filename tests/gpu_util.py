@@ -78,18 +78,46 @@ def upload(w, dev="cuda") -> DeviceWorkload:
 
 
 def gpu_step(dw: DeviceWorkload, partition_tokens: int = 0, write: bool = True, out=None):
-    from paged_kv_cache_75_amd import pa_decode, pa_write_kv
+    """pa_write_kv of the newest tokens (unless write=False), then pa_decode,
+    or pa_decode_partitioned when partition_tokens > 0."""
+    from paged_kv_cache_75_amd import pa_decode, pa_decode_partitioned, pa_write_kv
     if write:
         pa_write_kv(dw.new_k, dw.new_v, dw.slot_mapping, dw.k_pool, dw.v_pool)
+    if partition_tokens:
+        return pa_decode_partitioned(dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
+                                     dw.context_lens, dw.scale, partition_tokens, out=out,
+                                     max_context_len=dw.max_context_len)
     return pa_decode(dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens, dw.scale,
-                     out=out, max_context_len=dw.max_context_len,
-                     partition_tokens=partition_tokens)
+                     out=out, max_context_len=dw.max_context_len)
 
 
 def oracle_step(w, seqs=None, inplace=False):
     k, v = ref.write_kv(w.k_pool, w.v_pool, w.new_k, w.new_v, w.slot_mapping, w.block_size,
                         inplace=inplace)
     return ref.decode(w.q, k, v, w.block_tables, w.context_lens, w.scale, w.dtype, seqs=seqs), k, v
+
+
+# Half an output ulp at |o| in [2^e, 2^(e+1)) is HALF_ULP * 2^e: the error of
+# rounding a correctly computed result to the output type.
+HALF_ULP = {"f32": 2.0 ** -24, "f16": 2.0 ** -11, "bf16": 2.0 ** -8}
+# float32 accumulation error allowed on top of that rounding, relative to
+# max(1, |o|): far above what float32 sums of these lengths make, far below
+# any output ulp
+ACC_SLACK = 2.0 ** -14
+
+
+def element_bounds(want: np.ndarray, dtype: str):
+    """Per-element max-abs bound and the mask of elements where it is not the
+    stated bar.  The bar (1e-2 for fp16/bf16) holds everywhere except where
+    half an output ulp alone exceeds it (bf16 |o| >= 4, fp16 |o| >= 32): there
+    a correctly rounded output may differ by half an ulp, plus the float32
+    accumulation slack (which can also carry |o| into the next binade)."""
+    max_tol, _ = TOL[dtype]
+    slack = ACC_SLACK * np.maximum(1.0, np.abs(want))
+    mag = np.abs(want) + slack
+    half = HALF_ULP[dtype] * np.exp2(np.floor(np.log2(np.maximum(mag, 1e-30))))
+    wide = half > max_tol
+    return np.where(wide, half + slack, max_tol), wide
 
 
 def compare(got: np.ndarray, want: np.ndarray, dtype: str, seqs=None, label: str = ""):
@@ -100,13 +128,21 @@ def compare(got: np.ndarray, want: np.ndarray, dtype: str, seqs=None, label: str
     assert np.isfinite(got).all(), f"{label}: GPU output has non-finite values"
     err = np.abs(got - want)
     max_tol, mean_tol = TOL[dtype]
-    # one output ulp is the floor for elements whose magnitude alone puts the
-    # final rounding above the bar (|o| >= 4 in bf16); reported, not hidden
-    ulp = {"f32": 2.0 ** -23, "f16": 2.0 ** -10, "bf16": 2.0 ** -7}[dtype]
-    bound = np.maximum(max_tol, ulp * np.exp2(np.floor(np.log2(np.maximum(np.abs(want), 1e-30)))))
-    worst = float(err.max()) if err.size else 0.0
+    bound, wide = element_bounds(want, dtype)
+    narrow_err = err[~wide]
+    worst = float(narrow_err.max()) if narrow_err.size else 0.0
     mean = float(err.mean()) if err.size else 0.0
-    say(f"  {label}: max_abs={worst:.3e} mean_abs={mean:.3e} (bars {max_tol:g}/{mean_tol:g})")
-    assert (err <= bound).all(), f"{label}: max abs error {worst:.3e} > {max_tol}"
+    msg = f"  {label}: max_abs={worst:.3e} mean_abs={mean:.3e} (bars {max_tol:g}/{mean_tol:g})"
+    if wide.any():
+        # listed apart: elements whose half ulp exceeds the bar
+        msg += (f"; {int(wide.sum())} elements with half an ulp above the bar: "
+                f"max err {float(err[wide].max()):.3e}, max err/bound "
+                f"{float((err[wide] / bound[wide]).max()):.3f}")
+    say(msg)
+    bad = err > bound
+    assert not bad.any(), (
+        f"{label}: {int(bad.sum())} elements exceed their bound (max-abs {max_tol:g}; half an "
+        f"ulp + {ACC_SLACK:g}*max(1,|o|) where half an ulp is larger); worst error "
+        f"{float(err.max()):.3e} at |o|={float(np.abs(want)[np.unravel_index(err.argmax(), err.shape)]):.4g}")
     assert mean <= mean_tol, f"{label}: mean abs error {mean:.3e} > {mean_tol}"
     return worst, mean

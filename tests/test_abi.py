@@ -16,8 +16,9 @@ def test_exports_every_declared_function():
     assert {"pa_write_kv", "pa_decode", "pa_append_decode", "pa_decode_sliding", "pa_prefill",
             "pa_write_kv_fp8", "pa_decode_fp8", "pa_copy_blocks", "pa_bm_create",
             "pa_bm_allocate", "pa_bm_append", "pa_bm_fork", "pa_bm_free", "pa_bm_tables",
-            "pa_sha256", "pa_check_inputs", "pa_check_scratch_bytes", "pa_decode_workspace_bytes", "pa_profile_start", "pa_profile_stop",
-            "pa_status_string"} <= set(names)
+            "pa_sha256", "pa_check_inputs", "pa_check_scratch_bytes", "pa_decode_workspace_bytes",
+            "pa_decode_partitioned", "pa_decode_partitioned_workspace_bytes",
+            "pa_profile_start", "pa_profile_stop", "pa_status_string"} <= set(names)
     L = ctypes.CDLL(B.LIB_PATH)
     for n in names:
         assert hasattr(L, n), f"libpa.so does not export {n}"
@@ -39,12 +40,15 @@ FAKE = 0x1000    # never dereferenced: every call below fails validation first
 
 
 def decode(d, **kw):
+    """pa_decode, or pa_decode_partitioned when part= is given."""
     a = dict(q=FAKE, k=FAKE, v=FAKE, bt=FAKE, mb=8, cl=FAKE, n=4, maxlen=100, hq=8,
-             scale=0.1, out=FAKE, ws=FAKE, wsb=1 << 20, part=0)
+             scale=0.1, out=FAKE, ws=FAKE, wsb=1 << 20)
     a.update(kw)
-    return B.lib().pa_decode(a["q"], a["k"], a["v"], ctypes.byref(d) if d is not None else None,
-                             a["bt"], a["mb"], a["cl"], a["n"], a["maxlen"], a["hq"],
-                             a["scale"], a["out"], a["ws"], a["wsb"], a["part"], None)
+    args = (a["q"], a["k"], a["v"], ctypes.byref(d) if d is not None else None, a["bt"], a["mb"],
+            a["cl"], a["n"], a["maxlen"], a["hq"], a["scale"], a["out"], a["ws"], a["wsb"])
+    if "part" in a:
+        return B.lib().pa_decode_partitioned(*args, a["part"], None)
+    return B.lib().pa_decode(*args, None)
 
 
 @pytest.mark.parametrize("kw,bad_desc,want", [
@@ -59,6 +63,8 @@ def decode(d, **kw):
     (dict(out=None), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(part=24), None, B.PA_ERR_INVALID_ARGUMENT),        # not a multiple of 16
     (dict(part=16384), None, B.PA_ERR_UNSUPPORTED),
+    (dict(part=0), None, B.PA_ERR_INVALID_ARGUMENT),         # pa_decode is the library's split
+    (dict(part=-16), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(scale=float("nan")), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(maxlen=100, part=16, ws=None), None, B.PA_ERR_INVALID_ARGUMENT),
     (dict(maxlen=100, part=16, wsb=16), None, B.PA_ERR_WORKSPACE_TOO_SMALL),
@@ -112,15 +118,17 @@ def test_workspace_query():
     want = o_off + pieces * 4 * 128 * 4
     assert B.pa_decode_workspace_bytes(256, 32, d, 256) == want
     assert B.pa_decode_workspace_bytes(7, 32, d, 4096) == want
+    assert B.pa_decode_partitioned_workspace_bytes(7, 32, d, 4096, 0) == want
     # fixed partitions: one record per (seq, q head, partition); none for one partition
-    assert B.pa_decode_workspace_bytes(256, 32, d, 256, 256) == 0
-    got = B.pa_decode_workspace_bytes(256, 32, d, 4096, 256)
+    assert B.pa_decode_partitioned_workspace_bytes(256, 32, d, 256, 256) == 0
+    got = B.pa_decode_partitioned_workspace_bytes(256, 32, d, 4096, 256)
     rows = 256 * 32 * 16
     assert got == (rows * 128 * 4 + 255) // 256 * 256 + rows * 2 * 4
     # more sequences than the balanced split takes: fixed 256-token partitions
     rows = 1500 * 32 * 2
     assert B.pa_decode_workspace_bytes(1500, 32, d, 512) == (rows * 128 * 4 + 255) // 256 * 256 + rows * 8
     assert B.pa_decode_workspace_bytes(256, 31, d, 4096) == 0        # invalid -> 0
+    assert B.pa_decode_partitioned_workspace_bytes(256, 32, d, 4096, 24) == 0
 
 
 def append_decode(d, nk=FAKE, nv=FAKE, **kw):

@@ -20,6 +20,8 @@ def test_host_tensors_are_refused_everywhere():
     calls = {
         "pa_write_kv": lambda: B.pa_write_kv(nk, nk, cl, kp, vp),
         "pa_decode": lambda: B.pa_decode(q, kp, vp, bt, cl, 0.1, max_context_len=1),
+        "pa_decode_partitioned": lambda: B.pa_decode_partitioned(q, kp, vp, bt, cl, 0.1, 16,
+                                                                 max_context_len=1),
         "pa_decode_sliding": lambda: B.pa_decode_sliding(q, kp, vp, bt, cl, 0.1, 8,
                                                          max_context_len=1),
         "pa_append_decode": lambda: B.pa_append_decode(q, nk, nk, kp, vp, bt, cl, 0.1,

@@ -408,14 +408,12 @@ def test_sliding_window_full_size():
 
 def test_sliding_window_covering_everything_is_pa_decode():
     """W >= every T: the same bits as pa_decode, on both paths."""
-    from paged_kv_cache_75_amd import pa_decode, pa_decode_sliding
+    from paged_kv_cache_75_amd import pa_decode_sliding
     w = workloads.make(3, seed=1700, num_seqs=64)
     dw = upload(w, DEV)
     gpu_step(dw)                       # the newest tokens into the pools
     for part in (0, 256):
-        a = to_host(pa_decode(dw.q, dw.k_pool, dw.v_pool, dw.block_tables, dw.context_lens,
-                              dw.scale, max_context_len=dw.max_context_len,
-                              partition_tokens=part), w.dtype)
+        a = to_host(gpu_step(dw, partition_tokens=part, write=False), w.dtype)
         b = to_host(pa_decode_sliding(dw.q, dw.k_pool, dw.v_pool, dw.block_tables,
                                       dw.context_lens, dw.scale, w.max_context_len,
                                       max_context_len=dw.max_context_len,
