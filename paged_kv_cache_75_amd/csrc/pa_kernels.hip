@@ -897,14 +897,20 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
   const int lane = threadIdx.x;
   const int nrows = (N + kWave - 1) / kWave;
 
-  // ---- clamped lengths: every load in flight at once (lanes past the last
-  //      sequence repeat its load and count nothing) ----
+  // ---- clamped lengths: every load in flight at once, through a buffer
+  //      descriptor over the N lengths (a lane past the last sequence reads 0
+  //      without touching memory, so no branch separates the loads) ----
   int len[kRows];
+  {
+    const __amdgpu_buffer_rsrc_t lens = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<int32_t*>(a.context_lens), 0, N * 4, kBufferDword3);
 #pragma unroll
-  for (int r = 0; r < kRows; ++r) len[r] = a.context_lens[min(r * kWave + lane, N - 1)];
+    for (int r = 0; r < kRows; ++r)
+      len[r] = static_cast<int>(
+          __builtin_amdgcn_raw_buffer_load_b32(lens, (r * kWave + lane) * 4, 0, 0));
 #pragma unroll
-  for (int r = 0; r < kRows; ++r)
-    len[r] = r * kWave + lane < N ? min(max(len[r], 0), a.max_context_len) : 0;
+    for (int r = 0; r < kRows; ++r) len[r] = min(max(len[r], 0), a.max_context_len);
+  }
   // ---- pair units before each sequence: a scan over the lanes, row by row ----
   int pre[kRows];
   int carry = 0;

@@ -30,7 +30,7 @@ def _bytes(a):
 # the five configurations, full size
 # ---------------------------------------------------------------------------
 CASES = [(1, 1), (1, 101), (1, 102), (2, 2), (2, 101), (2, 102), (3, 3), (3, 101), (3, 102),
-         (4, 4), (5, 5), (5, 101), (5, 102)]
+         (4, 4), (4, 101), (4, 102), (5, 5), (5, 101), (5, 102)]
 
 
 @pytest.mark.parametrize("cfg,seed", CASES, ids=[f"cfg{c}-seed{s}" for c, s in CASES])
@@ -43,12 +43,62 @@ def test_config_parity(cfg, seed):
         f"B={w.block_size} max T={w.max_context_len})")
     out = gpu_step(dw)
     _sync()
-    seqs = [0, 21, 42, 63] if cfg == 4 else None
-    want, k_ref, v_ref = oracle_step(w, seqs=seqs, inplace=(cfg == 4))
-    compare(to_f64(out), want, w.dtype, seqs=seqs, label=f"config {cfg} seed {seed}")
+    say(f"[parity] config {cfg} seed {seed}: oracle, every sequence")
+    want, k_ref, v_ref = oracle_step(w, inplace=(cfg == 4))
+    compare(to_f64(out), want, w.dtype, label=f"config {cfg} seed {seed}")
     say(f"[parity] config {cfg} seed {seed}: pools after the write")
     assert np.array_equal(_bytes(to_host(dw.k_pool, w.dtype)), _bytes(k_ref))
     assert np.array_equal(_bytes(to_host(dw.v_pool, w.dtype)), _bytes(v_ref))
+    if cfg == 4:
+        # split-K at this shape: fixed partitions merged by the log-sum-exp
+        # reduce kernel (the balanced split gives each share one whole pair here)
+        for P in (256, 512, 1024):
+            say(f"[parity] config 4 seed {seed}: partitions of {P} tokens")
+            got = gpu_step(dw, partition_tokens=P, write=False)
+            _sync()
+            compare(to_f64(got), want, w.dtype, label=f"config 4 seed {seed} P={P}")
+
+
+def test_llama2_shape_with_cut_pairs():
+    """The config-4 head shape (32 kv heads, head_dim 128, fp16) with lengths
+    near 4096 that do not line up with the shares: every pair is cut into
+    pieces that the piece merge combines."""
+    lens = [4096 - 17 * i for i in range(16)]
+    w = workloads.random_paged("llama2-7b-cut", "f16", 32, 32, 128, 16, lens, seed=1300,
+                               spare_frac=0.05)
+    dw = upload(w, DEV)
+    say(f"[parity] llama2-7b shape, {len(lens)} seqs of {min(lens)}..{max(lens)} tokens")
+    out = gpu_step(dw)
+    _sync()
+    want, _, _ = oracle_step(w)
+    compare(to_f64(out), want, w.dtype, label="llama2-7b cut pairs")
+
+
+def test_more_sequences_than_the_balanced_split_takes():
+    """1100 sequences (over the balanced split's 1024): pa_decode falls back
+    to fixed 256-token partitions and matches the oracle."""
+    rng = np.random.default_rng(1310)
+    lens = rng.integers(1, 400, 1100).tolist()
+    w = workloads.random_paged("many-seqs", "bf16", 32, 8, 128, 16, lens, seed=1311)
+    dw = upload(w, DEV)
+    say(f"[parity] {len(lens)} sequences, default path")
+    out = gpu_step(dw)
+    _sync()
+    want, _, _ = oracle_step(w)
+    compare(to_f64(out), want, w.dtype, label="1100 sequences")
+
+
+def test_long_contexts():
+    """Contexts of 32k and 64k tokens (and short ones beside them) on the
+    balanced split: a pair spans dozens of shares."""
+    lens = [65536, 32768, 32769, 40000, 7, 1]
+    w = workloads.random_paged("long", "bf16", 32, 8, 128, 16, lens, seed=1320)
+    dw = upload(w, DEV)
+    say(f"[parity] long contexts {lens}")
+    out = gpu_step(dw)
+    _sync()
+    want, _, _ = oracle_step(w)
+    compare(to_f64(out), want, w.dtype, label="long contexts")
 
 
 # ---------------------------------------------------------------------------
@@ -134,6 +184,30 @@ def test_shapes(dtype, head_dim, group):
     want, _, _ = oracle_step(w)
     got = to_f64(out)
     compare(got, want, dtype, label=f"{dtype} D={head_dim} G={group}")
+    assert np.array_equal(got[9], np.zeros_like(got[9])), "T = 0 must give zeros"
+
+
+BALANCED_SHAPES = [(dt, d, g) for dt in ("f16", "bf16") for d in (64, 128)
+                   for g in (1, 2, 3, 4, 5, 6, 7, 8, 16)]
+
+
+@pytest.mark.parametrize("dtype,head_dim,group", BALANCED_SHAPES,
+                         ids=[f"{a}-d{b}-g{c}" for a, b, c in BALANCED_SHAPES])
+def test_shapes_balanced_split(dtype, head_dim, group):
+    """The shapes on pa_decode's default path (the balanced split), with
+    lengths that put several pairs, partial tiles and empty sequences in one
+    share and cut long pairs into pieces."""
+    hkv = 2
+    lens = [1, 2, 15, 16, 17, 33, 100, 257, 300, 0, 511, 1500]
+    w = workloads.random_paged("shape-bal", dtype, hkv * group, hkv, head_dim, 16, lens,
+                               seed=350 + group, spare_frac=0.3, max_blocks=100)
+    dw = upload(w, DEV)
+    say(f"[shape, balanced] {dtype} D={head_dim} G={group}")
+    out = gpu_step(dw)
+    _sync()
+    want, _, _ = oracle_step(w)
+    got = to_f64(out)
+    compare(got, want, dtype, label=f"balanced {dtype} D={head_dim} G={group}")
     assert np.array_equal(got[9], np.zeros_like(got[9])), "T = 0 must give zeros"
 
 
