@@ -146,6 +146,26 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                     void* stream);
 
 /*
+ * pa_decode_noalloc -- pa_decode for callers that cannot allocate device
+ * memory (code under HIP graph capture, serving loops or harnesses that
+ * forbid allocation).  Arguments, results and errors are pa_decode's, without
+ * the workspace: the library keeps one fixed workspace of 36 MiB per GPU, in
+ * device memory reserved when the library's code is loaded on that GPU and
+ * held until the process ends, and the call allocates and frees nothing.
+ * Sizes whose pa_decode_workspace_bytes exceeds 36 MiB (e.g. 16 query heads
+ * per kv head at head_dim 128) return PA_ERR_UNSUPPORTED.  Every call on a GPU
+ * uses that GPU's one workspace: calls that may overlap on one GPU (other
+ * streams, other threads) race and must be ordered by the caller.  Nothing in
+ * the workspace needs clearing between calls.  The kernel timing of
+ * pa_profile_start creates events, so it must be off around these calls.
+ */
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, void* out, void* stream);
+
+/*
  * pa_decode_partitioned -- pa_decode with fixed context partitions: every
  * sequence's context is cut into partitions of partition_tokens tokens (a
  * multiple of 16, 16 .. 8192); one workgroup attends over one partition of

@@ -24,7 +24,8 @@ missing; nothing falls back to another implementation.
 from .binding import (BlockManager, OutOfBlocks, PoolSet, pa_check_inputs, pa_copy_blocks, pa_sha256, PA_BF16, PA_ERR_HIP, PA_ERR_INVALID_ARGUMENT, PA_ERR_UNSUPPORTED,
                       PA_ERR_WORKSPACE_TOO_SMALL, PA_F16, PA_F32, PA_OK, PaError, lib,
                       fp8_pool_desc, pa_append_decode, pa_append_decode_fp8, pa_decode, pa_decode_fp8,
-                      pa_decode_partitioned, pa_decode_partitioned_workspace_bytes,
+                      pa_decode_noalloc, pa_decode_partitioned,
+                      pa_decode_partitioned_workspace_bytes,
                       pa_decode_sliding, pa_decode_workspace_bytes, pa_pool_desc, pa_prefill,
                       pa_profile_start, pa_profile_stop, pa_status_string, pa_stream_read,
                       pa_write_kv,
@@ -33,7 +34,7 @@ from .binding import (BlockManager, OutOfBlocks, PoolSet, pa_check_inputs, pa_co
 __all__ = ["BlockManager", "OutOfBlocks", "PoolSet", "pa_check_inputs", "pa_copy_blocks", "pa_sha256", "PA_BF16", "PA_ERR_HIP", "PA_ERR_INVALID_ARGUMENT", "PA_ERR_UNSUPPORTED",
            "PA_ERR_WORKSPACE_TOO_SMALL", "PA_F16", "PA_F32", "PA_OK", "PaError", "lib",
            "fp8_pool_desc", "pa_append_decode", "pa_append_decode_fp8", "pa_decode",
-           "pa_decode_fp8", "pa_decode_partitioned", "pa_decode_partitioned_workspace_bytes",
+           "pa_decode_fp8", "pa_decode_noalloc", "pa_decode_partitioned", "pa_decode_partitioned_workspace_bytes",
            "pa_decode_sliding", "pa_decode_workspace_bytes", "pa_pool_desc", "pa_prefill",
            "pa_profile_start", "pa_profile_stop", "pa_status_string", "pa_stream_read",
            "pa_write_kv",

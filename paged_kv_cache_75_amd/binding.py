@@ -76,6 +76,8 @@ def lib():
                        vp, vp, sz, vp], c_int),
         "pa_decode_partitioned": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
                                    vp, vp, sz, i32, vp], c_int),
+        "pa_decode_noalloc": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
+                               vp, vp], c_int),
         "pa_decode_sliding": ([vp, vp, vp, desc, vp, i32, vp, i32, i32, i32, ctypes.c_float,
                                i32, vp, vp, sz, i32, vp], c_int),
         "pa_append_decode": ([vp, vp, vp, vp, vp, desc, vp, i32, vp, i32, i32, i32,
@@ -372,6 +374,37 @@ def pa_decode(q, k_pool, v_pool, block_tables, context_lens, scale, out=None, *,
     from torch's caching allocator."""
     return _decode(q, None, None, k_pool, v_pool, block_tables, context_lens, scale, out,
                    max_context_len, workspace, 0, stream)
+
+
+def pa_decode_noalloc(q, k_pool, v_pool, block_tables, context_lens, scale, out, *,
+                      max_context_len, stream=None):
+    """pa_decode on the library's own per-GPU workspace: the call allocates
+    nothing (``out`` must be given).  Calls that may overlap on one GPU race."""
+    torch = _torch()
+    _on_current_device(k_pool, "k_pool")
+    desc = pool_desc(k_pool)
+    dev = k_pool.device
+    _check(k_pool, "k_pool")
+    _check(v_pool, "v_pool", dtype=k_pool.dtype, device=dev)
+    if v_pool.shape != k_pool.shape:
+        raise ValueError("k_pool and v_pool differ in shape")
+    _check(q, "q", dtype=k_pool.dtype, dim=3, device=dev)
+    _check(block_tables, "block_tables", dtype=torch.int32, dim=2, device=dev)
+    _check(context_lens, "context_lens", dtype=torch.int32, dim=1, device=dev)
+    _check(out, "out", dtype=q.dtype, device=dev)
+    n, hq, d = (int(x) for x in q.shape)
+    if d != desc.head_dim or tuple(out.shape) != tuple(q.shape):
+        raise ValueError("q / out shapes disagree with the pool")
+    if int(block_tables.shape[0]) != n or int(context_lens.shape[0]) != n:
+        raise ValueError("block_tables / context_lens rows must equal num_seqs")
+    st = lib().pa_decode_noalloc(q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+                                 ctypes.byref(desc), block_tables.data_ptr(),
+                                 int(block_tables.shape[1]), context_lens.data_ptr(), n,
+                                 int(max_context_len), hq, float(scale), out.data_ptr(),
+                                 _stream(stream))
+    if st != PA_OK:
+        raise PaError(st, "pa_decode_noalloc")
+    return out
 
 
 def pa_decode_partitioned(q, k_pool, v_pool, block_tables, context_lens, scale,

@@ -206,6 +206,25 @@ pa_status pa_decode(const void* q, const void* k_pool, const void* v_pool,
                 workspace_bytes, 0, 0, stream);
 }
 
+pa_status pa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                            const pa_pool_desc* pool, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t num_seqs, int32_t max_context_len, int32_t num_q_heads,
+                            float scale, void* out, void* stream) {
+  pa::DecodePlan plan;
+  const pa_status s = pa::plan_decode(num_seqs, num_q_heads, pool, max_context_len,
+                                      max_blocks_per_seq, 0, &plan);
+  if (s != PA_OK) return s;
+  if (plan.ws_bytes > pa::kStaticScratchBytes) return PA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0 && num_seqs > 0) {
+    if (pa::static_scratch(&ws) != hipSuccess) return PA_ERR_HIP;
+  }
+  return decode(q, nullptr, nullptr, k_pool, v_pool, pool, block_tables, max_blocks_per_seq,
+                context_lens, num_seqs, max_context_len, num_q_heads, scale, out, ws,
+                pa::kStaticScratchBytes, 0, 0, stream);
+}
+
 pa_status pa_decode_partitioned(const void* q, const void* k_pool, const void* v_pool,
                                 const pa_pool_desc* pool, const int32_t* block_tables,
                                 int32_t max_blocks_per_seq, const int32_t* context_lens,

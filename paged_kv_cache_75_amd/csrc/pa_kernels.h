@@ -126,6 +126,11 @@ hipError_t launch_stream_read(const void* buf, int64_t bytes, uint32_t* sink, hi
 void profile_start();
 hipError_t profile_stop(int32_t* launches, double* mean_us);
 
+// Size of the library-held decode workspace (pa_decode_noalloc) and the
+// current device's copy of it (its address is looked up once per device).
+constexpr size_t kStaticScratchBytes = size_t(36) << 20;
+hipError_t static_scratch(void** ptr);
+
 // dtype is a pa_dtype value; head_dim 64/128; group as planned.
 hipError_t launch_decode(const DecodeArgs& a, int32_t dtype, int32_t head_dim,
                          int32_t group, hipStream_t stream);

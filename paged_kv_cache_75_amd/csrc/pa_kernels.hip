@@ -1731,6 +1731,35 @@ hipError_t launch_decode_dt(const DecodeArgs& a, int32_t head_dim, int32_t group
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Library-held decode workspace for callers that cannot allocate
+// (pa_decode_noalloc).  One copy per GPU, living until the process ends.  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device may reach a
+// kernel or a copy.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
+
+hipError_t static_scratch(void** ptr) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;          // device -> that device's copy
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(mu);
+  const auto it = addr.find(dev);
+  if (it != addr.end()) {
+    *ptr = it->second;
+    return hipSuccess;
+  }
+  void* p = nullptr;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  addr[dev] = p;
+  *ptr = p;
+  return hipSuccess;
+}
+
 KernelTimer& kernel_timer() {
   static KernelTimer t;
   return t;
