@@ -3,28 +3,31 @@
  * bookkeeping that decides which physical block of the KV pools each token
  * of each sequence lives in.  Plain host code; no call touches the GPU.
  *
- * What it implements ("vLLM Framework and Inference Engine Design",
- * vineetganti.com, section "How is vLLM's KV cache paged?"):
+ * State and transitions (policies from "vLLM Framework and Inference Engine
+ * Design", vineetganti.com, sections "How is vLLM's KV cache paged?" and
+ * "What operations can cause memory fragmentation, and how does vLLM avoid
+ * it?"; the hash from sudo.vn, "vLLM self-hosted LLM", section "Prefix
+ * caching: reusing the KV of identical prefixes"):
  *
- *   - Growing: when a sequence's last block is full, a block is taken from
- *     the free list and appended to its block table.  Nothing is copied.
- *   - Sharing: every block has a reference count.  With prefix caching a
- *     full block is also named by a hash of its own tokens and every token
- *     before it; a new sequence whose prompt starts the same way reuses
- *     those blocks and the caller skips that much prefill.
- *   - Freeing: when a sequence ends each of its blocks loses a reference; a
- *     block at zero returns to the free list but keeps its hash, so it can
- *     still be hit until its space is needed.  Least recently used blocks
- *     are reused first.
- *   - Copy-on-write (same page, section "What operations can cause memory
- *     fragmentation, and how does vLLM avoid it?"): a sequence about to
- *     write into a block that other sequences share gets a fresh block
- *     instead; the caller copies the old block into it (pa_copy_blocks)
- *     before the write.  Forked sequences share partial blocks this way.
- *   - Hash (sudo.vn, "vLLM self-hosted LLM", section "Prefix caching:
- *     reusing the KV of identical prefixes"): only full blocks are hashed,
- *     each hash chains on the previous block's, SHA-256, and a per-request
- *     salt keeps requests with different salts from sharing.
+ *   - per block: a reference count, an optional digest, and a place in an
+ *     LRU queue while its count is zero;
+ *   - per sequence: its block list (the block table), token count and the
+ *     token ids of its partial last block;
+ *   - append: a token that starts a new block takes the queue's head block
+ *     (dropping any digest it held); a token that completes a block gives the
+ *     block its digest; no KV is ever moved to grow a sequence;
+ *   - allocate with prefix caching: leading full prompt blocks whose digests
+ *     are registered are taken with one more reference each (a hit on a
+ *     queued block takes it out of the queue);
+ *   - release: every block of the sequence drops one reference; blocks that
+ *     reach zero join the queue's tail still holding their digest, so they
+ *     remain hittable until reused;
+ *   - copy-on-write: writing into a last block whose count is above one
+ *     moves the writer to a fresh block and reports the (old, new) pair for
+ *     pa_copy_blocks, which the caller runs before the write; fork is how
+ *     partial blocks come to be shared;
+ *   - digests: SHA-256 chained through the parent block's digest, over full
+ *     blocks only, seeded by a per-request salt.
  *
  * Conventions:
  *

@@ -9,76 +9,23 @@ CPU-baseline leg of ``bench.py`` may import it; the library never imports it
 and it imports nothing from the library.  Plain Python lists and dicts, with
 ``hashlib.sha256`` as the one library primitive; pools are NumPy arrays.
 
-What it follows, page by page:
+What it follows (the pages fix the policies; the byte layout of a hash and the
+tie-breaking orders are readings, listed below):
 
 * "vLLM Framework and Inference Engine Design" (vineetganti.com), section
-  "How is vLLM's KV cache paged?": a sequence grows by taking a block from a
-  free list when its last block is full and appending it to its block table,
-  copying nothing; every block carries a reference count; with prefix caching
-  a full block is also named by a hash of its own tokens and of all tokens
-  before it, so a request whose prompt begins the same way reuses the blocks
-  and skips that much prefill; when a request ends each of its blocks loses a
-  reference, a block at zero goes back to the free list but keeps its hash
-  and can still be hit until its space is needed, and the least recently
-  used blocks are reused first.
+  "How is vLLM's KV cache paged?": growth by whole blocks from a free list,
+  with nothing copied; reference counts on blocks; prefix caching that names
+  a full block by a hash covering its tokens and every token before them;
+  release that decrements counts and parks zero-count blocks, digest intact,
+  for least-recently-used reuse.
 * Same page, section "What operations can cause memory fragmentation, and how
-  does vLLM avoid it?": every block has the same size, so any free block
-  serves any request; reference counts let requests with a common prefix
-  share blocks; the original design copies a shared block only when a
-  sequence has to write into it (copy-on-write), while the V1 engine shares
-  only full blocks, which are never written again.
+  does vLLM avoid it?": equal-size blocks (any free block serves any
+  request), sharing through reference counts, and copy-on-write of a shared
+  block at the first write into it (the V1 engine shares only full blocks).
 * sudo.vn, "vLLM self-hosted LLM", section "Prefix caching: reusing the KV of
-  identical prefixes": only full blocks are cached; a block's hash is made
-  from the previous block's hash, the block's token ids and extra values such
-  as a cache salt, so it stands for the whole prefix; SHA-256 is the default
-  hash; blocks nobody references sit in a free queue and are evicted least
-  recently used first; a salt restricts sharing to requests with that salt.
-* bibekananda.in, "vLLM", section "The part that is easy to miss": requests
-  with a common prefix point at the same blocks and the engine counts the
-  references; a request that writes past the shared region gets fresh blocks
-  of its own and the shared ones are left untouched.
-
-Readings taken where the pages leave a step open:
-
-* Hash input: the parent's 32-byte digest followed by the block's token ids
-  as little-endian int32.  The first block's parent is the SHA-256 of the
-  salt bytes (the empty string when there is no salt), so every hashed
-  message has the same length and two prefixes collide only through a
-  SHA-256 collision.
-* Only full blocks get a hash, when they become full: at allocation for the
-  full blocks of a prompt, on the append that fills a block.  The first
-  block registered under a hash keeps the name; a later block with an equal
-  hash holds the hash but is not registered (it can be hit only by its own
-  sequence's table).
-* Prefix match: the longest run of leading full prompt blocks whose hashes
-  are registered, capped so that at least one prompt token is left to
-  compute (the step must still produce the last prompt token's output).
-* Free queue: block ids in ascending order at start; allocation takes the
-  head; a block whose count drops to zero joins the tail.  A request's blocks
-  are released last block first, so its later blocks are reused before its
-  earlier ones (a hit on a block needs hits on every block before it).  A
-  hit on a block with count zero takes it out of the queue; a block taken
-  from the head for new tokens loses its hash (eviction).
-* Fork (the original design's sharing, e.g. parallel samples of one prompt):
-  the child shares every block of the parent, the partial last block too.
-* Append: a token that starts a new block takes a free block.  Otherwise, if
-  the last block is shared (count > 1), copy-on-write: a free block is taken,
-  the whole old block is copied into it (reported as a (source, destination)
-  pair for the copy kernel) and the old block loses one reference.
-* An operation that needs more free blocks than there are fails and changes
-  nothing.  Unknown or duplicate sequence ids are errors.
-* Block copy: ``pool[dst] = pool[src]`` for every pair, all pools, whole
-  blocks, raw bytes, every source read before any destination is written.
-  Destinations are distinct and are not sources (a copy-on-write destination
-  is always a fresh block).
-
-Parity pins (tests/test_oracle_pins.py): the pages' worked examples (three
-prompts sharing a system prompt match 0, 10 and 10 blocks of 16 tokens; the
-fragmentation example's 2,016 paged slots; twelve requests sharing an
-1,800-token prefix), brute-force invariants over random operation sequences,
-the chain property of the hash, salt isolation, LRU reuse after free, and the
-decode-through-a-copied-block invariance.  No function here is "parity
-unpinned".
+  identical prefixes": hashes over full blocks only, each chained on its
+  parent's and including extra keys such as a salt; SHA-256; an LRU queue
+  of unreferenced blocks; sharing limited to requests with the same salt.
 """
 
 from __future__ import annotations

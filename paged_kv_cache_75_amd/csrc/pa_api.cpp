@@ -186,6 +186,14 @@ pa_status decode(const void* q, const void* new_k, const void* new_v, const void
   a.new_k = new_k;
   a.new_v = new_v;
   a.window = window;
+  // keys and values stream past the caches when the batch may read more than
+  // the 256 MB Infinity Cache holds (its KV bytes are at most num_seqs x
+  // max_context_len rows of every kv head); smaller batches keep the default
+  // policy, so blocks that sequences share are read once from memory
+  const double kv_bound = double(num_seqs) * double(max_context_len) * 2.0 *
+                          double(pool->num_kv_heads) * double(pool->head_dim) *
+                          (kv_fp8 ? 1.0 : double(pa::dtype_bytes(pool->dtype)));
+  a.kv_stream = kv_bound > double(pa::kInfinityCacheBytes) ? 1 : 0;
   const hipError_t e = pa::launch_decode(a, pool->dtype, pool->head_dim, plan.group,
                                          static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PA_OK : PA_ERR_HIP;

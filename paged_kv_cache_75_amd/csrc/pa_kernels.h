@@ -65,6 +65,9 @@ struct DecodeArgs {
   int32_t kv_fp8;
   float v_scale;
   float k_scale;            // FP8 pools: the key scale itself (appended rows are quantized)
+  // Balanced split: load keys and values non-temporally (batches larger than
+  // the Infinity Cache); 0 keeps the default cache policy
+  int32_t kv_stream;
 };
 
 hipError_t launch_write_kv(const WriteArgs& a, hipStream_t stream);

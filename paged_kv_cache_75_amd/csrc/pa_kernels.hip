@@ -815,34 +815,28 @@ constexpr int kMetaStore = 0x40;   // ... and its table entry lies in the pool
 
 constexpr int kPairCost = 1;
 
-// Share sizes by the parity of the workgroup index.  Workgroup i runs on XCD
-// i mod 8, and on MI355X the odd XCD of each even/odd pair streams these
-// reads about 6% slower (per-XCD wave end times over full-size batches:
-// odd/even 1.04-1.08, whichever shares the XCDs are given), so odd shares
-// are made that much smaller.  The split stays a fixed function of the
-// lengths, so results do not depend on timing.
-constexpr int kEvenWeight = 33;
-constexpr int kOddWeight = 31;
+// Cache policy of the key and value loads when the batch streams (the host
+// sets DecodeArgs::kv_stream for batches whose KV bytes may exceed the 256 MB
+// Infinity Cache): non-temporal (the "nt" bit).  Reads of shuffled 4 KiB
+// tiles measured 12% faster so, and the eight XCDs finished together (with
+// the default policy the odd XCD of each pair finished about 6% later).
+// Smaller batches keep the default policy: blocks that several sequences
+// share (a common prefix) are then read from the caches after the first read.
+constexpr int kStreamLoad = 2;
 
 __device__ inline int pair_units(int T, int window) {
   const int tiles = attended_tiles(T, window);
   return tiles ? tiles + kPairCost : 0;
 }
 
-__device__ inline long long share_weight(int w) {
-  return static_cast<long long>(w >> 1) * (kEvenWeight + kOddWeight) + ((w & 1) ? kEvenWeight : 0);
-}
-// first unit of share w of nsh (total units < 2^31)
+// first unit of share w of nsh equal shares (total units < 2^31)
 __device__ inline int share_lo(int total, int w, int nsh) {
-  return static_cast<int>(static_cast<long long>(total) * share_weight(w) / share_weight(nsh));
+  return static_cast<int>(static_cast<long long>(total) * w / nsh);
 }
-// the share holding unit u < total
+// the share holding unit u < total: the largest w with share_lo(w) <= u,
+// i.e. total * w < (u + 1) * nsh, so w = ceil((u + 1) * nsh / total) - 1
 __device__ inline int share_of(int total, int u, int nsh) {
-  int w = static_cast<int>(static_cast<long long>(u) * nsh / total);
-  w = min(w, nsh - 1);
-  while (w + 1 < nsh && share_lo(total, w + 1, nsh) <= u) ++w;
-  while (w > 0 && share_lo(total, w, nsh) > u) --w;
-  return w;
+  return static_cast<int>(((static_cast<long long>(u) + 1) * nsh + total - 1) / total) - 1;
 }
 
 template <int DT, int D, int G, bool kAppend>
@@ -1126,7 +1120,10 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         kr.r.k[kk] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(rk, k_off + 64 * kk - shift, 0, 0));
+            uint4, a.kv_stream ? __builtin_amdgcn_raw_buffer_load_b128(
+                                     rk, k_off + 64 * kk - shift, 0, kStreamLoad)
+                               : __builtin_amdgcn_raw_buffer_load_b128(
+                                     rk, k_off + 64 * kk - shift, 0, 0));
       kr.meta = meta;
       kr.off = off;
     };
@@ -1139,8 +1136,10 @@ __global__ __launch_bounds__(kWave) void decode_stream_kernel(DecodeArgs a) {
 #pragma unroll
       for (int s2 = 0; s2 < VS; ++s2)
         vr.v[s2] = __builtin_bit_cast(
-            uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                       rv, v_off + s2 * RPI * kPoolRowBytes - shift, 0, 0));
+            uint4, a.kv_stream ? __builtin_amdgcn_raw_buffer_load_b128(
+                                     rv, v_off + s2 * RPI * kPoolRowBytes - shift, 0, kStreamLoad)
+                               : __builtin_amdgcn_raw_buffer_load_b128(
+                                     rv, v_off + s2 * RPI * kPoolRowBytes - shift, 0, 0));
     };
     // Appending tile: the newest row of the keys and of the values comes from
     // the segment's LDS copy of new_k / new_v (register selects only, so the

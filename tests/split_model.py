@@ -4,7 +4,7 @@ Test infrastructure.  It replays, with Python integers, what every wave of
 ``decode_stream_kernel`` (``paged_kv_cache_75_amd/csrc/pa_kernels.hip``)
 works out before it reads the pools: the units of each (sequence, kv head)
 pair (its attended 16-token tiles plus one for the pair's fixed cost), the
-share bounds (weighted by the parity of the workgroup index), the runs of
+equal share bounds, the runs of
 segments the lanes find in parallel (at most ``seg_cap`` per run, at most 64
 candidate sequences per search), each segment's tiles and piece flags, and the
 piece headers the merge kernel reads.  It holds no attention arithmetic and is
@@ -20,7 +20,6 @@ import dataclasses
 
 TILE = 16
 PAIR_COST = 1
-EVEN_WEIGHT, ODD_WEIGHT = 33, 31
 WAVE = 64
 PIECE_FIRST, PIECE_LAST, SHARE_FIRST = 1, 2, 4
 
@@ -38,21 +37,13 @@ def pair_units(T: int, window: int) -> int:
     return t + PAIR_COST if t else 0
 
 
-def share_weight(w: int) -> int:
-    return (w >> 1) * (EVEN_WEIGHT + ODD_WEIGHT) + (EVEN_WEIGHT if w & 1 else 0)
-
-
 def share_lo(total: int, w: int, nsh: int) -> int:
-    return total * share_weight(w) // share_weight(nsh)
+    return total * w // nsh
 
 
 def share_of(total: int, u: int, nsh: int) -> int:
-    w = min(u * nsh // total, nsh - 1)
-    while w + 1 < nsh and share_lo(total, w + 1, nsh) <= u:
-        w += 1
-    while w > 0 and share_lo(total, w, nsh) > u:
-        w -= 1
-    return w
+    """The largest w with share_lo(w) <= u, in closed form."""
+    return ((u + 1) * nsh + total - 1) // total - 1
 
 
 @dataclasses.dataclass

@@ -26,3 +26,17 @@ def test_help_names_every_mode():
     assert r.returncode == 0
     for flag in ("--prefill", "--window", "--fp8", "--cow", "--step", "--copy-calibration"):
         assert flag in r.stdout
+
+
+def test_cpu_baseline_runs_on_the_small_workload():
+    """The oracle's timed leg (all cores, then one core), on the host alone,
+    plain, with a window and with FP8 pools."""
+    sys.path.insert(0, ROOT)
+    import bench
+    import workloads
+    w = workloads.make(1, seed=1, poison=False)
+    for window, fp8 in ((0, None), (8, None), (0, (4.0 / 448, 4.0 / 448))):
+        kv = bench.kv_bytes_per_step(w, window) // (w.elem_bytes if fp8 else 1)
+        all_tbps, cores, one_tbps, sample = bench.cpu_baseline(w, 0.4, kv, window, fp8)
+        assert all_tbps > 0 and one_tbps > 0 and 1 <= cores <= 16
+        assert "one core" in sample
