@@ -207,12 +207,21 @@ def summary_traffic(path, sources):
 DECODE_SOURCES = ("pa_device.h", "pa_kernels.hip")
 WINDOW_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_sliding_llama3-8b-w256-bf16.json")
 FP8_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_fp8_llama3-8b-e4m3.json")
+C4_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_llama2-7b-f16.json")
+C5_PROFILE_SUMMARY = os.path.join(ROOT, "profiles", "decode_stream_prefix-shared-bf16.json")
 
 
-def profiled_summary(cfg, fused, window, fp8):
+def profiled_summary(cfg, fused, window, fp8, partition):
     """The committed counter summary of the attention kernel a bench line
     measures, for the workloads that were profiled (configuration 3: the
-    appending step, the 256-token window, FP8 pools), else None."""
+    appending step, the 256-token window, FP8 pools; configuration 4;
+    configuration 5's appending step), else None."""
+    if partition:
+        return None
+    if cfg == 4 and not (window or fp8):
+        return C4_PROFILE_SUMMARY
+    if cfg == 5 and fused and not (window or fp8):
+        return C5_PROFILE_SUMMARY
     if cfg != 3:
         return None
     if fp8:
@@ -719,7 +728,7 @@ def main():
     achieved = roof_bytes / (kernel_us * 1e-6) / 1e9
     value = kv_bytes / (ms_per_step * 1e-3) / 1e12
 
-    summary = profiled_summary(cfg, fused, args.window, args.fp8)
+    summary = profiled_summary(cfg, fused, args.window, args.fp8, args.partition)
     traffic_bytes, prof = summary_traffic(summary, DECODE_SOURCES) if summary else (None, None)
     traffic = None if traffic_bytes is None else round(traffic_bytes)
     result = {
