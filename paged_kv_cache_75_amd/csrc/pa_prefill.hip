@@ -84,26 +84,43 @@ __device__ __forceinline__ int seq_of_rank(const DecodeArgs& a, int k, int& len)
 // weights does not depend on their scale.
 constexpr float kRefSlack = 8.0f;
 
-// x rounded to the nearest element value (ties to even), as a float; x is a
-// finite weight in [0, 1]
-template <int DT> __device__ inline float round_to_elem(float x);
-template <> __device__ inline float round_to_elem<PA_BF16>(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return __uint_as_float((u + 0x7fffu + ((u >> 16) & 1u)) & 0xffff0000u);
+// The maximum over a column's four lanes (gq = 0..3) with gfx950's
+// NaN-propagating maximum (scores are finite or -inf here): unlike fmaxf it
+// needs no quieting of the values the lane swaps bring in.
+__device__ __forceinline__ float column_maximum(float x) {
+  const auto p = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = __builtin_elementwise_maximum(__uint_as_float(p[0]), __uint_as_float(p[1]));
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __builtin_elementwise_maximum(__uint_as_float(q[0]), __uint_as_float(q[1]));
 }
-template <> __device__ inline float round_to_elem<PA_F16>(float x) {
-  return static_cast<float>(static_cast<_Float16>(x));
+
+// Eight element-type ones: the A operand whose product with the weights gives
+// every row of the result the column's sum of the weights.
+template <int DT> __device__ inline uint4 ones_chunk();
+template <> __device__ inline uint4 ones_chunk<PA_BF16>() {
+  return make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u);
+}
+template <> __device__ inline uint4 ones_chunk<PA_F16>() {
+  return make_uint4(0x3c003c00u, 0x3c003c00u, 0x3c003c00u, 0x3c003c00u);
 }
 
 // One 16-column block of a prefill wave: Q^T operand, O^T accumulators, the
-// running reference and sum, and the step's weights.
+// running reference and sum, and the step's weights.  The sum is a product
+// on the matrix cores, (all-ones)^T . P^T beside V^T . P^T: every entry of `l`
+// holds the column's sum of the same rounded weights that enter P.V, so the
+// result is an exact weighted average of the value rows with those weights
+// (its rounding error then scales with how far the values lie from the
+// result, not with their size), and no vector instruction adds them.
 template <int DT, int D>
 struct PrefillCols {
   static constexpr int KK = D / 32;            // 32-element chunks of a query row
   static constexpr int NT = D / 16;            // 16-row tiles of O^T
   uint4 qb[KK];
   f32x4 o[NT];
-  float m_run, l_run;
+  f32x4 l;
+  float m_run;
   float p[8];                                  // keys 4gq + i of each 16-key half
 };
 
@@ -126,20 +143,22 @@ __device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
 }
 
 // The step's weights for every column block from its raw scores (S^T =
-// K . Q^T per half): scaled, masked on diagonal steps, column maxima, then
-// one wave-uniform test for a reference move in any block, then the weights.
+// K . Q^T per half; the query rows carry the sign of the scale, so `scale` is
+// its magnitude in log2 units): masked on diagonal steps, column maxima of the
+// raw scores, scaled, then one wave-uniform test for a reference move in any
+// block, then the weights exp2(raw * scale - m) with the scale inside the FMA.
 template <int DT, int D, int NB>
-__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB],
-                                                  const DecodeArgs& a, const f32x4 (&sc)[NB][2],
-                                                  int gq, bool mask, const int (&live)[NB][2]) {
+__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB], float scale,
+                                                  const f32x4 (&sc)[NB][2], int gq, bool mask,
+                                                  const int (&live)[NB][2]) {
   float s[NB][8], mx[NB];
   bool move = false;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s[b][i] = sc[b][0][i] * a.scale_log2;
-      s[b][4 + i] = sc[b][1][i] * a.scale_log2;
+      s[b][i] = sc[b][0][i];
+      s[b][4 + i] = sc[b][1][i];
     }
     // keys after a column's position (a wave-uniform branch: steps on the
     // diagonal only)
@@ -150,10 +169,13 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
         if (4 * gq + i >= live[b][1]) s[b][4 + i] = -INFINITY;
       }
     }
-    float m = -INFINITY;
+    float m = s[b][0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, s[b][i]);
-    mx[b] = column_max(m);
+    for (int i = 1; i < 8; ++i) m = __builtin_elementwise_maximum(m, s[b][i]);
+    m = column_maximum(m);
+    // scaling is monotonic (scale >= 0), so this is the maximum of the
+    // scaled scores; -inf (nothing live) stays -inf when the scale is 0
+    mx[b] = m == -INFINITY ? -INFINITY : m * scale;
     move |= mx[b] > cols[b].m_run + kRefSlack;
   }
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -165,25 +187,21 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
 #pragma unroll
       for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
-      t.l_run *= alpha;
+      t.l *= alpha;
       t.m_run = m_new;
     }
   }
-  // The weights enter P.V rounded to the element type; the sum l adds the
-  // same rounded weights, so the result is an exact weighted average of the
-  // value rows with those weights (its error from the rounding then scales
-  // with how far the values lie from the result, not with their size).
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     PrefillCols<DT, D>& t = cols[b];
     const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
-    float psum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      t.p[i] = round_to_elem<DT>(__builtin_amdgcn_exp2f(s[b][i] - m_use));
-      psum += t.p[i];
+    for (int i = 0; i < 8; ++i) t.p[i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale, -m_use));
+    // a masked key's exponent is -inf, or NaN when the scale is 0
+    if (mask) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) t.p[i] = s[b][i] == -INFINITY ? 0.0f : t.p[i];
     }
-    t.l_run += psum;
   }
 }
 
@@ -232,6 +250,8 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], lds
 #pragma unroll
     for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
   }
+#pragma unroll
+  for (int b = 0; b < NB; ++b) cols[b].l = mfma_chunk<DT>(ones_chunk<DT>(), pb[b], cols[b].l);
 }
 
 template <int DT, int D, int G, bool kTileInBlock>
@@ -282,6 +302,8 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
 
   PC cols[NB];
   const int gq = lane >> 4, c = lane & 15;
+  const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
+  const float scale = fabsf(a.scale_log2);
   bool col_ok[NB];
   int pos[NB];
   int64_t out_row[NB];
@@ -295,12 +317,15 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     const uint4* qrow = reinterpret_cast<const uint4*>(static_cast<const char*>(a.q) +
                                                        out_row[b] * kRowBytes);
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk)
-      cols[b].qb[kk] = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+    for (int kk = 0; kk < KK; ++kk) {
+      const uint4 v = col_ok[b] ? qrow[4 * kk + gq] : make_uint4(0, 0, 0, 0);
+      // the scale's sign moves into the query (exact: a sign flip)
+      cols[b].qb[kk] = make_uint4(v.x ^ qsign, v.y ^ qsign, v.z ^ qsign, v.w ^ qsign);
+    }
 #pragma unroll
     for (int n = 0; n < PC::NT; ++n) cols[b].o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    cols[b].l = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     cols[b].m_run = -INFINITY;
-    cols[b].l_run = 0.0f;
   }
 
   // the wave's first position; a wave with no queries computes columns it
@@ -438,7 +463,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][0] = min(kTileTokens, max(0, before));
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
-    prefill_softmax32<DT, D, NB>(cols, a, cur, gq, mask, live);
+    prefill_softmax32<DT, D, NB>(cols, scale, cur, gq, mask, live);
     accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
   };
 
@@ -457,10 +482,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
 
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-    // column c's sum is spread over its four lanes (gq = 0..3)
-    float l = cols[b].l_run;
-    l += __shfl_xor(l, 16, kWave);
-    l += __shfl_xor(l, 32, kWave);
+    const float l = cols[b].l[0];
     if (col_ok[b]) {
       const float inv = 1.0f / l;
 #pragma unroll
