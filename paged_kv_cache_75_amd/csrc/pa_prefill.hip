@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cfloat>
 #include <cstdint>
 
 #include "pa_device.h"
@@ -142,16 +143,19 @@ __device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
   }
 }
 
-// The step's weights for every column block from its raw scores (S^T =
-// K . Q^T per half; the query rows carry the sign of the scale, so `scale` is
-// its magnitude in log2 units): masked on diagonal steps, column maxima of the
-// raw scores, scaled, then one wave-uniform test for a reference move in any
-// block, then the weights exp2(raw * scale - m) with the scale inside the FMA.
+// A step's softmax for every column block from its raw scores (S^T = K . Q^T
+// per half; the query rows carry the sign of the scale, so `scale` is its
+// magnitude in log2 units), in two parts.  The reference: mask on diagonal
+// steps, column maxima of the raw scores, scaled, then one wave-uniform test
+// for a reference move in any block (and the rescale when one moves).  The
+// weights: exp2(raw * scale - m) with the scale inside the FMA.  Between the
+// two the next step's score products are issued, so that they run on the
+// matrix cores while the weights are computed.
 template <int DT, int D, int NB>
-__device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB], float scale,
-                                                  const f32x4 (&sc)[NB][2], int gq, bool mask,
-                                                  const int (&live)[NB][2]) {
-  float s[NB][8], mx[NB];
+__device__ __forceinline__ void prefill_reference(PrefillCols<DT, D> (&cols)[NB], float scale,
+                                                  float (&s)[NB][8], const f32x4 (&sc)[NB][2],
+                                                  int gq, bool mask, const int (&live)[NB][2]) {
+  float mx[NB];
   bool move = false;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
@@ -173,9 +177,9 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
 #pragma unroll
     for (int i = 1; i < 8; ++i) m = __builtin_elementwise_maximum(m, s[b][i]);
     m = column_maximum(m);
-    // scaling is monotonic (scale >= 0), so this is the maximum of the
-    // scaled scores; -inf (nothing live) stays -inf when the scale is 0
-    mx[b] = m == -INFINITY ? -INFINITY : m * scale;
+    // scaling is monotonic (scale > 0), so this is the maximum of the
+    // scaled scores
+    mx[b] = m * scale;
     move |= mx[b] > cols[b].m_run + kRefSlack;
   }
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
@@ -191,17 +195,19 @@ __device__ __forceinline__ void prefill_softmax32(PrefillCols<DT, D> (&cols)[NB]
       t.m_run = m_new;
     }
   }
+}
+
+// A masked key's raw score is -inf, so its exponent is -inf and its weight 0
+// (the scale is at least FLT_MIN, never 0).
+template <int DT, int D, int NB>
+__device__ __forceinline__ void prefill_weights(PrefillCols<DT, D> (&cols)[NB], float scale,
+                                                const float (&s)[NB][8]) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     PrefillCols<DT, D>& t = cols[b];
     const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
 #pragma unroll
     for (int i = 0; i < 8; ++i) t.p[i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale, -m_use));
-    // a masked key's exponent is -inf, or NaN when the scale is 0
-    if (mask) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) t.p[i] = s[b][i] == -INFINITY ? 0.0f : t.p[i];
-    }
   }
 }
 
@@ -303,7 +309,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   PC cols[NB];
   const int gq = lane >> 4, c = lane & 15;
   const uint32_t qsign = a.scale_log2 < 0.0f ? 0x80008000u : 0u;
-  const float scale = fabsf(a.scale_log2);
+  // a zero scale is taken as FLT_MIN: every finite score times it rounds
+  // away against the reference, so the weights are the same (all 1 before
+  // normalisation), and a masked key's -inf stays -inf instead of NaN
+  const float scale = fmaxf(fabsf(a.scale_log2), FLT_MIN);
   bool col_ok[NB];
   int pos[NB];
   int64_t out_row[NB];
@@ -450,7 +459,6 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       }
     }
     __syncthreads();
-    if (st + 1 < wave_steps) qk(st + 1, next);
     if (st >= wave_steps) return;
     // masking is needed unless every key of the step precedes every
     // column's position
@@ -463,7 +471,12 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][0] = min(kTileTokens, max(0, before));
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
-    prefill_softmax32<DT, D, NB>(cols, scale, cur, gq, mask, live);
+    float sr[NB][8];
+    prefill_reference<DT, D, NB>(cols, scale, sr, cur, gq, mask, live);
+    // the next step's scores (computed also after a wave's last step, from
+    // whatever its stage holds, and then unused: one branch less per step)
+    qk(st + 1, next);
+    prefill_weights<DT, D, NB>(cols, scale, sr);
     accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
   };
 
