@@ -92,21 +92,11 @@ template <> __device__ inline void store4<PA_F16>(void* base, int64_t idx, f32x4
   *reinterpret_cast<h4*>(static_cast<_Float16*>(base) + idx) = h;
 }
 template <> __device__ inline void store4<PA_BF16>(void* base, int64_t idx, f32x4 x) {
-  uint16_t* p = static_cast<uint16_t*>(base) + idx;
-  uint32_t w[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    uint16_t h[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t u = __float_as_uint(x[2 * i + j]);
-      h[j] = ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu))
-                 ? static_cast<uint16_t>((u >> 16) | 0x0040u)
-                 : static_cast<uint16_t>((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
-    }
-    w[i] = uint32_t(h[0]) | (uint32_t(h[1]) << 16);
-  }
-  *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+  // round to nearest even (gfx950 converts a pair per instruction; NaN stays NaN)
+  typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+  const b4 h = {static_cast<__bf16>(x[0]), static_cast<__bf16>(x[1]), static_cast<__bf16>(x[2]),
+                static_cast<__bf16>(x[3])};
+  *reinterpret_cast<b4*>(static_cast<__bf16*>(base) + idx) = h;
 }
 
 // ---------------------------------------------------------------------------
