@@ -122,6 +122,7 @@ struct PrefillCols {
   f32x4 o[NT];
   f32x4 l;
   float m_run;
+  float lim;                                   // raw-score bound of the reference test
   float p[8];                                  // keys 4gq + i of each 16-key half
 };
 
@@ -144,55 +145,56 @@ __device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
 }
 
 // A step's softmax for every column block from its raw scores (S^T = K . Q^T
-// per half; the query rows carry the sign of the scale, so `scale` is its
-// magnitude in log2 units), in two parts.  The reference: mask on diagonal
-// steps, column maxima of the raw scores, scaled, then one wave-uniform test
-// for a reference move in any block (and the rescale when one moves).  The
-// weights: exp2(raw * scale - m) with the scale inside the FMA.  Between the
-// two the next step's score products are issued, so that they run on the
+// per half, lane (gq, c) holding keys 4gq .. 4gq+3 of each half; the query
+// rows carry the sign of the scale, so `scale` is its magnitude in log2
+// units), in two parts.  The reference: mask on diagonal steps (in place),
+// then one wave-uniform test whether any lane's raw maximum exceeds its
+// column's bound `lim` (the reference plus kRefSlack, in raw units); only then
+// are the column maxima formed and the reference moved, with the rescale.
+// The weights: exp2(raw * scale - m) with the scale inside the FMA.  Between
+// the two the next step's score products are issued, so that they run on the
 // matrix cores while the weights are computed.
 template <int DT, int D, int NB>
 __device__ __forceinline__ void prefill_reference(PrefillCols<DT, D> (&cols)[NB], float scale,
-                                                  float (&s)[NB][8], const f32x4 (&sc)[NB][2],
-                                                  int gq, bool mask, const int (&live)[NB][2]) {
+                                                  f32x4 (&sc)[NB][2], int gq, bool mask,
+                                                  const int (&live)[NB][2]) {
   float mx[NB];
   bool move = false;
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s[b][i] = sc[b][0][i];
-      s[b][4 + i] = sc[b][1][i];
-    }
     // keys after a column's position (a wave-uniform branch: steps on the
     // diagonal only)
     if (mask) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (4 * gq + i >= live[b][0]) s[b][i] = -INFINITY;
-        if (4 * gq + i >= live[b][1]) s[b][4 + i] = -INFINITY;
+        if (4 * gq + i >= live[b][0]) sc[b][0][i] = -INFINITY;
+        if (4 * gq + i >= live[b][1]) sc[b][1][i] = -INFINITY;
       }
     }
-    float m = s[b][0];
+    float m = sc[b][0][0];
 #pragma unroll
-    for (int i = 1; i < 8; ++i) m = __builtin_elementwise_maximum(m, s[b][i]);
-    m = column_maximum(m);
-    // scaling is monotonic (scale > 0), so this is the maximum of the
-    // scaled scores
-    mx[b] = m * scale;
-    move |= mx[b] > cols[b].m_run + kRefSlack;
+    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][0][i]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][1][i]);
+    mx[b] = m;
+    move |= m > cols[b].lim;
   }
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
       PrefillCols<DT, D>& t = cols[b];
-      const float m_new = fmaxf(t.m_run, mx[b]);
+      // scaling is monotonic (scale > 0): the column's maximum of the scaled
+      // scores; -inf when nothing is live yet
+      const float cm = column_maximum(mx[b]) * scale;
+      const float m_new = fmaxf(t.m_run, cm);
       // a column with nothing so far (m_new = -inf) has nothing to rescale
       const float alpha = m_new == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(t.m_run - m_new);
 #pragma unroll
       for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) t.o[n] *= alpha;
       t.l *= alpha;
       t.m_run = m_new;
+      // raw scores above this take a weight above 2^kRefSlack
+      t.lim = m_new == -INFINITY ? -INFINITY : (m_new + kRefSlack) / scale;
     }
   }
 }
@@ -201,13 +203,16 @@ __device__ __forceinline__ void prefill_reference(PrefillCols<DT, D> (&cols)[NB]
 // (the scale is at least FLT_MIN, never 0).
 template <int DT, int D, int NB>
 __device__ __forceinline__ void prefill_weights(PrefillCols<DT, D> (&cols)[NB], float scale,
-                                                const float (&s)[NB][8]) {
+                                                const f32x4 (&sc)[NB][2]) {
 #pragma unroll
   for (int b = 0; b < NB; ++b) {
     PrefillCols<DT, D>& t = cols[b];
     const float m_use = t.m_run == -INFINITY ? 0.0f : t.m_run;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) t.p[i] = __builtin_amdgcn_exp2f(fmaf(s[b][i], scale, -m_use));
+    for (int i = 0; i < 4; ++i) {
+      t.p[i] = __builtin_amdgcn_exp2f(fmaf(sc[b][0][i], scale, -m_use));
+      t.p[4 + i] = __builtin_amdgcn_exp2f(fmaf(sc[b][1][i], scale, -m_use));
+    }
   }
 }
 
@@ -335,6 +340,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     for (int n = 0; n < PC::NT; ++n) cols[b].o[n] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     cols[b].l = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     cols[b].m_run = -INFINITY;
+    cols[b].lim = -INFINITY;
   }
 
   // the wave's first position; a wave with no queries computes columns it
@@ -471,12 +477,11 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][0] = min(kTileTokens, max(0, before));
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
-    float sr[NB][8];
-    prefill_reference<DT, D, NB>(cols, scale, sr, cur, gq, mask, live);
+    prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
     // the next step's scores (computed also after a wave's last step, from
     // whatever its stage holds, and then unused: one branch less per step)
     qk(st + 1, next);
-    prefill_weights<DT, D, NB>(cols, scale, sr);
+    prefill_weights<DT, D, NB>(cols, scale, cur);
     accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
   };
 
