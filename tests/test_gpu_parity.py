@@ -101,6 +101,24 @@ def test_long_contexts():
     compare(to_f64(out), want, w.dtype, label="long contexts")
 
 
+@pytest.mark.parametrize("n,cap,seed", [(251, 32, 251), (1024, 20, 9)])
+def test_many_short_sequences_balanced_split(n, cap, seed):
+    """Hundreds of short contexts (1..cap tokens) on the balanced split: a
+    share holds many segments, so it takes several runs, and a run may end on
+    a pair's fixed-cost unit (the case a run could once finish with no
+    segment).  pa_decode and pa_append_decode against the oracle."""
+    rng = np.random.default_rng(seed)
+    lens = rng.integers(1, cap + 1, n).tolist()
+    w = workloads.random_paged(f"short-{n}", "bf16", 32, 8, 128, 16, lens, seed=seed + 1)
+    dw = upload(w, DEV)
+    say(f"[parity] {n} sequences of 1..{cap} tokens, pa_decode")
+    out = gpu_step(dw)
+    _sync()
+    want, _, _ = oracle_step(w)
+    compare(to_f64(out), want, w.dtype, label=f"{n} short sequences")
+    _check_append(w, 0, f"{n} short sequences, appending")
+
+
 # ---------------------------------------------------------------------------
 # slot write
 # ---------------------------------------------------------------------------
