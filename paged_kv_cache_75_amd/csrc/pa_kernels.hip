@@ -1474,37 +1474,52 @@ __global__ __launch_bounds__((MergeShape<G, D>::kThreads)) void merge_pieces_ker
       const float w1 = np > 1 ? l1 * __builtin_amdgcn_exp2f(m1 - M) : 0.0f;
       float L = w0 + w1;
       f32x4 O = w0 * o0 + w1 * o1;
-      // the rest, kBatch at a time (all loads in flight together)
-      for (int p0 = 2; p0 < np; p0 += kBatch) {
+      // the rest, kBatch at a time, folded in a fixed order; the next
+      // batch's loads are issued before the current batch is folded, so a
+      // pair of many pieces costs one round trip per batch less
+      struct Batch {
         float m[kBatch], l[kBatch];
         f32x4 o[kBatch];
+      };
+      auto load = [&](Batch& bt, int p0) {
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
           const int p = p0 + b;
           if (p < np) {
             const float* ml = piece_ml(2 * (w + p), h);
-            m[b] = ml[0];
-            l[b] = ml[1];
-            o[b] = piece_o(2 * (w + p), qd);
+            bt.m[b] = ml[0];
+            bt.l[b] = ml[1];
+            bt.o[b] = piece_o(2 * (w + p), qd);
           } else {
-            m[b] = -INFINITY;
-            l[b] = 0.0f;
-            o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            bt.m[b] = -INFINITY;
+            bt.l[b] = 0.0f;
+            bt.o[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
           }
         }
+      };
+      auto fold = [&](const Batch& bt) {
         float Mb = M;
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) Mb = fmaxf(Mb, m[b]);
+        for (int b = 0; b < kBatch; ++b) Mb = fmaxf(Mb, bt.m[b]);
         const float f = __builtin_amdgcn_exp2f(M - Mb);
         L *= f;
         O *= f;
 #pragma unroll
         for (int b = 0; b < kBatch; ++b) {
-          const float wgt = l[b] * __builtin_amdgcn_exp2f(m[b] - Mb);
+          const float wgt = bt.l[b] * __builtin_amdgcn_exp2f(bt.m[b] - Mb);
           L += wgt;
-          O += wgt * o[b];
+          O += wgt * bt.o[b];
         }
         M = Mb;
+      };
+      Batch ba, bb;
+      if (np > 2) load(ba, 2);
+      for (int p0 = 2; p0 < np; p0 += 2 * kBatch) {
+        if (p0 + kBatch < np) load(bb, p0 + kBatch);
+        fold(ba);
+        if (p0 + kBatch >= np) break;
+        if (p0 + 2 * kBatch < np) load(ba, p0 + 2 * kBatch);
+        fold(bb);
       }
       store4<DT>(a.out, row0 * D + 4 * qd, O * (1.0f / L));
     }

@@ -18,7 +18,7 @@ constexpr int32_t kMaxPartitionTokens = 8192;
 // share (smaller batches use fewer workgroups).
 constexpr int32_t kMaxSplits = 4096;
 constexpr int32_t kMaxSplitSeqs = 1024;
-constexpr int32_t kMinSplitTiles = 16;
+constexpr int32_t kMinSplitTiles = 8;
 // MI355X's Infinity Cache (the memory-side cache in front of HBM)
 constexpr int64_t kInfinityCacheBytes = int64_t(256) << 20;
 // Chunked prefill: 16-column query blocks per wave, and the XCDs whose L2s a

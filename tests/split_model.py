@@ -66,7 +66,7 @@ class Split:
 
 
 def model(lens, num_kv_heads: int, max_context_len: int, num_waves: int, seg_cap: int,
-          window: int = 0, min_split_tiles: int = 16) -> Split:
+          window: int = 0, min_split_tiles: int = 8) -> Split:
     """The split every wave of a launch with ``num_waves`` workgroups computes."""
     N, Hkv = len(lens), num_kv_heads
     T = [min(max(int(t), 0), max_context_len) for t in lens]
