@@ -130,7 +130,8 @@ size_t pa_decode_workspace_bytes(int32_t num_seqs, int32_t num_q_heads,
  * How the context is split across workgroups is the library's choice: for
  * fp16/bf16 pools with a block size of at least 16, the flattened work of all
  * (sequence, kv head) pairs, in 16-token tiles, is cut into equal contiguous
- * shares, one per resident wave (at most 1024 sequences); otherwise fixed
+ * shares, one per resident wave but none under 8 tiles (at most 1024
+ * sequences); otherwise fixed
  * 256-token partitions (pa_decode_partitioned with 256).  Pieces of a pair
  * computed by different workgroups are merged by log-sum-exp in a second
  * kernel; the split depends only on the sizes and context_lens, so a call
