@@ -234,15 +234,29 @@ struct PrefillLds {
   static constexpr int kStageBytes = kValOffset + kStepRows * kValStride;
 };
 
-// O^T += V^T . P^T over a 32-key step for every column block.  The step's 32
-// value rows sit in LDS at the padded stride; `rbase` points at lane (gq,
-// c)'s first read: row 4gq + c/4 of the first half, dimensions 4(c%4) .. +3.
-// A transposed read gives the lane four keys of one dimension, 4gq .. 4gq+3
-// of a half, and the read 16 rows further on the same four keys of the
-// second half: together the A operand chunk matching the weights' order.
-template <int DT, int D, int NB>
-__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], lds_char* rbase) {
+// O^T += V^T . P^T over a 32-key step for every column block, in two parts:
+// read_v32 reads the A operand chunks, accumulate32 does the products.  The
+// step's 32 value rows sit in LDS at the padded stride; `rbase` points at
+// lane (gq, c)'s first read: row 4gq + c/4 of the first half, dimensions
+// 4(c%4) .. +3.  A transposed read gives the lane four keys of one
+// dimension, 4gq .. 4gq+3 of a half, and the read 16 rows further on the
+// same four keys of the second half: together the A operand chunk matching
+// the weights' order.
+template <int DT, int D, int NT>
+__device__ __forceinline__ void read_v32(uint4 (&av)[NT], lds_char* rbase) {
   constexpr int kValStride = PrefillLds<DT, D>::kValStride;
+#pragma unroll
+  for (int n = 0; n < NT; ++n) {
+    lds_char* at = rbase + 32 * n;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
+    const v4i16 hi =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kValStride));
+    const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
+    av[n] = make_uint4(l.x, l.y, h.x, h.y);
+  }
+}
+template <int DT, int D, int NB, int NT>
+__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const uint4 (&avs)[NT]) {
   // two four-element halves as one eight-element operand chunk
   auto join = [](v4i16 lo, v4i16 hi) {
     const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
@@ -252,12 +266,8 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], lds
 #pragma unroll
   for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
 #pragma unroll
-  for (int n = 0; n < PrefillCols<DT, D>::NT; ++n) {
-    lds_char* at = rbase + 32 * n;
-    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)at);
-    const v4i16 hi =
-        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(at + kTileTokens * kValStride));
-    const uint4 av = join(lo, hi);
+  for (int n = 0; n < NT; ++n) {
+    const uint4 av = avs[n];
 #pragma unroll
     for (int b = 0; b < NB; ++b) cols[b].o[n] = mfma_chunk<DT>(av, pb[b], cols[b].o[n]);
   }
@@ -395,6 +405,38 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     const int64_t blk = min(max(table[t >> lb], 0), nblk - 1);
     return blk * blk_rows + head_rows + (t & bmask);
   };
+  // tiles inside blocks: the rows of step st go from memory straight into
+  // LDS stage st % kStages, one 4-byte-per-lane load per row (the row lands
+  // at its padded place; rows past T, and a tile past the last position,
+  // read as zeros).  Wave w moves step rows 8w .. 8w + 7 of the keys and of
+  // the values, which lie in one tile.
+  constexpr int kRowsPerWave = kStepRows / kPrefillWaves;
+  constexpr int kRowLanes = kRowBytes / 4;
+  static_assert(kRowsPerWave * kPrefillWaves == kStepRows && kTileTokens % kRowsPerWave == 0 &&
+                    kRowLanes <= kWave,
+                "direct row loads");
+  // byte offset of step st's LDS stage, unsigned so that the compiler can
+  // fold each read's constant part into the instruction's offset field
+  auto stage_of = [](int st) -> uint32_t { return uint32_t(st) % kStages * kStageBytes; };
+  auto load_rows = [&](int st) {
+    const int r0 = wave * kRowsPerWave;
+    const int k = 2 * st + r0 / kTileTokens;
+    const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, k), rv = rsrc(vbase, k);
+    lds_char* const sb = (lds_char*)lds + stage_of(st);
+    if (lane < kRowLanes) {
+#pragma unroll
+      for (int i = 0; i < kRowsPerWave; ++i) {
+        const int sr = r0 + i;
+        const int off = (sr % kTileTokens) * kRowBytes + 4 * lane;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, sb + sr * LS::kKeyStride, 4, off, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, sb + LS::kValOffset + sr * LS::kValStride, 4,
+                                                 off, 0, 0, 0);
+      }
+    }
+  };
+  // every wave's rows in LDS before the barrier that lets the others read them
+  auto rows_landed = [] { __builtin_amdgcn_s_waitcnt(0x0f70); };   // vmcnt(0)
+  // blocks smaller than a tile: staged through registers
   struct Stage {
     uint4 k[kLoads], v[kLoads];
   };
@@ -402,18 +444,9 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
       const int sr = i * kLoadRows + lrow;                 // row of the step
-      if constexpr (kTileInBlock) {
-        const int k = 2 * st + load_half(i);
-        const int off = (sr % kTileTokens) * kRowBytes + lchunk * 16;
-        r.k[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsrc(kbase, k), off, 0, 0));
-        r.v[i] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                               rsrc(vbase, k), off, 0, 0));
-      } else {
-        const int64_t row = row_of(st * kStepRows + sr);
-        r.k[i] = reinterpret_cast<const uint4*>(kbase + row * kRowBytes)[lchunk];
-        r.v[i] = reinterpret_cast<const uint4*>(vbase + row * kRowBytes)[lchunk];
-      }
+      const int64_t row = row_of(st * kStepRows + sr);
+      r.k[i] = reinterpret_cast<const uint4*>(kbase + row * kRowBytes)[lchunk];
+      r.v[i] = reinterpret_cast<const uint4*>(vbase + row * kRowBytes)[lchunk];
     }
   };
   auto store_step = [&](const Stage& r, char* st) {
@@ -433,39 +466,56 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   lds_char* const lds_v = (lds_char*)lds + LS::kValOffset +
                           (4 * gq + (c >> 2)) * LS::kValStride + ((c & 1) << 3) +
                           (((c & 3) >> 1) << 4);
-  // byte offset of step st's LDS stage, unsigned so that the compiler can
-  // fold each read's constant part into the instruction's offset field
-  auto stage_of = [](int st) -> uint32_t { return uint32_t(st) % kStages * kStageBytes; };
-  // S^T of a step for every column block (keys from the step's LDS stage)
+  // S^T of a step for every column block: the key fragments from the step's
+  // LDS stage (lane (gq, c): key row c of each half, chunks 4kk + gq), then
+  // the products
   using Scores = f32x4[NB][2];
-  auto qk = [&](int st, Scores& sc) {
-    const char* kt = lds + stage_of(st);
-    // lane (gq, c): key row c of each half, chunks 4kk + gq
-    const char* kb = kt + c * LS::kKeyStride + gq * 16;
-    KeyRegs<DT, D> kr[2];
+  using Keys = KeyRegs<DT, D>[2];
+  auto read_k = [&](int st, Keys& kr) {
+    const char* kb = lds + stage_of(st) + c * LS::kKeyStride + gq * 16;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
         kr[h].k[kk] = *reinterpret_cast<const uint4*>(kb + h * kTileTokens * LS::kKeyStride +
                                                       64 * kk);
+  };
+  auto qk = [&](const Keys& kr, Scores& sc) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) prefill_qk32<DT, D>(cols[b], kr[0], kr[1], sc[b][0], sc[b][1]);
   };
-  // Step st: stage the rows of step st + 1 and fetch those of st + 2; after
-  // the barrier, step st + 1's rows are complete too, so its scores go to the
-  // matrix cores before step st's softmax and P.V (`cur` holds step st's
-  // scores, `next` receives step st + 1's).
+  // Step st.  After the barrier every stage up to st + 1 is complete: the
+  // wave reads this step's value fragments and the next step's key
+  // fragments, only then requests the rows of step st + 2 (into the stage
+  // step st - 1 used, which every wave has left), and computes: step st's
+  // softmax reference, step st + 1's score products, the weights and P.V
+  // (`cur` holds step st's scores, `next` receives step st + 1's).  With
+  // blocks smaller than a tile the rows of step st + 1 are staged from
+  // registers before the barrier instead.
   auto step = [&](int st, Scores& cur, Scores& next) {
-    if (st + 1 < nsteps) {
+    if constexpr (kTileInBlock) {
+      rows_landed();
+    } else if (st + 1 < nsteps) {
       store_step(R, lds + stage_of(st + 1));
-      if (st + 2 < nsteps) {
-        if (kTileInBlock && ((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
-        load_step(st + 2, R);
-      }
+      if (st + 2 < nsteps) load_step(st + 2, R);
     }
     __syncthreads();
-    if (st >= wave_steps) return;
+    const bool computes = st < wave_steps;
+    Keys kr;
+    uint4 avs[PC::NT];
+    if (computes) {
+      // the next step's keys (past the last step: whatever the stage holds,
+      // unused), this step's values
+      read_k(st + 1, kr);
+      read_v32<DT, D, PC::NT>(avs, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
+    }
+    if constexpr (kTileInBlock) {
+      if (st + 2 < nsteps) {
+        if (((2 * st + 4) & 63) == 0) load_tbl((2 * st + 4) >> 6);
+        load_rows(st + 2);
+      }
+    }
+    if (!computes) return;
     // masking is needed unless every key of the step precedes every
     // column's position
     const bool mask = (st + 1) * kStepRows - 1 > first_pos;
@@ -478,20 +528,28 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
     prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
-    // the next step's scores (computed also after a wave's last step, from
-    // whatever its stage holds, and then unused: one branch less per step)
-    qk(st + 1, next);
+    qk(kr, next);
     prefill_weights<DT, D, NB>(cols, scale, cur);
-    accumulate32<DT, D, NB>(cols, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
+    accumulate32<DT, D, NB, PC::NT>(cols, avs);
   };
 
-  if constexpr (kTileInBlock) load_tbl(0);
-  load_step(0, R);
-  store_step(R, lds);
-  if (nsteps > 1) load_step(1, R);
+  if constexpr (kTileInBlock) {
+    load_tbl(0);
+    load_rows(0);
+    if (nsteps > 1) load_rows(1);
+    rows_landed();
+  } else {
+    load_step(0, R);
+    store_step(R, lds);
+    if (nsteps > 1) load_step(1, R);
+  }
   __syncthreads();
   Scores SA, SB;
-  if (wave_steps > 0) qk(0, SA);
+  if (wave_steps > 0) {
+    Keys k0;
+    read_k(0, k0);
+    qk(k0, SA);
+  }
   for (int st = 0; st < nsteps; st += 2) {
     step(st, SA, SB);
     if (st + 1 >= nsteps) break;
