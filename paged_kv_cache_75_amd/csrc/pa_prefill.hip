@@ -26,13 +26,14 @@ namespace {
 // (its per-lane `live` bound).
 //
 // The workgroup walks the keys in 32-key steps up to its last position.  Each
-// step's key and value rows are loaded once, every thread taking a few 16-byte
-// chunks, and staged in LDS, where all the waves' column blocks read them:
-// keys as the A operand of S^T = K . Q^T (row-wise reads), values through
-// transposed reads for O^T += V^T . P^T (rows padded: PrefillLds).  Three LDS
-// stages and one barrier per step: the rows of step s + 1 are written while
-// step s is computed, and a stage is rewritten only after every wave has
-// passed the barrier that follows its last reader.
+// step's key and value rows are loaded once into LDS, where all the waves'
+// column blocks read them: keys as the A operand of S^T = K . Q^T (row-wise
+// reads), values through transposed reads for O^T += V^T . P^T (rows padded:
+// PrefillLds).  When tiles lie inside blocks the rows go from memory straight
+// into LDS (LDS-direct buffer loads, one row per instruction); smaller blocks
+// stage them through registers.  Three LDS stages and one barrier per step:
+// a stage is rewritten only after every wave has passed the barrier that
+// follows its last reader.
 //
 // Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
 // own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
