@@ -30,10 +30,13 @@ namespace {
 // column blocks read them: keys as the A operand of S^T = K . Q^T (row-wise
 // reads), values through transposed reads for O^T += V^T . P^T (rows padded:
 // PrefillLds).  When tiles lie inside blocks the rows go from memory straight
-// into LDS (LDS-direct buffer loads, one row per instruction); smaller blocks
-// stage them through registers.  Three LDS stages and one barrier per step:
-// a stage is rewritten only after every wave has passed the barrier that
-// follows its last reader.
+// into LDS (LDS-direct buffer loads, one row per instruction), and a step's
+// P.V products are issued at the start of the next step, ahead of that step's
+// softmax reference, so that each wave's matrix and vector work overlap; the
+// values are then read a step later, so four LDS stages rotate.  Smaller
+// blocks stage the rows through registers, with three stages and P.V in its
+// own step.  One barrier per step: a stage is rewritten only after every wave
+// has passed the barrier that follows its last reader.
 //
 // Workgroup order: workgroup i runs on XCD i mod kXcds, and each XCD has its
 // own L2.  All query blocks of one (sequence, kv head) pair go to one XCD, a
@@ -256,16 +259,22 @@ __device__ __forceinline__ void read_v32(uint4 (&av)[NT], lds_char* rbase) {
     av[n] = make_uint4(l.x, l.y, h.x, h.y);
   }
 }
-template <int DT, int D, int NB, int NT>
-__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const uint4 (&avs)[NT]) {
+// The step's weights of every column block as B operand chunks (rounded to
+// the element type), and the products with the value chunks `avs` (and with
+// all-ones for the sums).
+template <int DT, int D, int NB>
+__device__ __forceinline__ void pack_weights(const PrefillCols<DT, D> (&cols)[NB], uint4 (&pb)[NB]) {
   // two four-element halves as one eight-element operand chunk
   auto join = [](v4i16 lo, v4i16 hi) {
     const uint2 l = __builtin_bit_cast(uint2, lo), h = __builtin_bit_cast(uint2, hi);
     return make_uint4(l.x, l.y, h.x, h.y);
   };
-  uint4 pb[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) pb[b] = join(pack4<DT>(cols[b].p), pack4<DT>(cols[b].p + 4));
+}
+template <int DT, int D, int NB, int NT>
+__device__ __forceinline__ void accumulate_packed(PrefillCols<DT, D> (&cols)[NB], const uint4 (&avs)[NT],
+                                                  const uint4 (&pb)[NB]) {
 #pragma unroll
   for (int n = 0; n < NT; ++n) {
     const uint4 av = avs[n];
@@ -274,6 +283,12 @@ __device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], con
   }
 #pragma unroll
   for (int b = 0; b < NB; ++b) cols[b].l = mfma_chunk<DT>(ones_chunk<DT>(), pb[b], cols[b].l);
+}
+template <int DT, int D, int NB, int NT>
+__device__ __forceinline__ void accumulate32(PrefillCols<DT, D> (&cols)[NB], const uint4 (&avs)[NT]) {
+  uint4 pb[NB];
+  pack_weights<DT, D, NB>(cols, pb);
+  accumulate_packed<DT, D, NB, NT>(cols, avs, pb);
 }
 
 template <int DT, int D, int G, bool kTileInBlock>
@@ -291,7 +306,10 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   constexpr int kLoads = kStepRows / kLoadRows;           // per matrix and step
   using LS = PrefillLds<DT, D>;
   constexpr int kStageBytes = LS::kStageBytes;            // keys, then values
-  constexpr int kStages = 3;
+  // Tiles inside blocks: a step's P.V waits for the next step (deferred), so
+  // a stage is read until the step after its own and four stages rotate.
+  constexpr bool kDeferPV = kTileInBlock;
+  constexpr int kStages = kDeferPV ? 4 : 3;
   static_assert(kThreads % CPR == 0 && kStepRows % kLoadRows == 0 &&
                     (kLoadRows % kTileTokens == 0 || kTileTokens % kLoadRows == 0),
                 "load shape");
@@ -493,6 +511,19 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   // (`cur` holds step st's scores, `next` receives step st + 1's).  With
   // blocks smaller than a tile the rows of step st + 1 are staged from
   // registers before the barrier instead.
+  //
+  // Deferred P.V (tiles inside blocks): step st issues the products of step
+  // st - 1's weights (held packed in pb) with that step's values first, then
+  // its own softmax reference on the vector units while the matrix cores
+  // work, so one wave overlaps the two.  The sums are the same and in the
+  // same order: step st - 1's products are added before step st may rescale.
+  // A wave computes one step past its last (wholly masked: its weights are
+  // zero) to add its last products, or adds them after the loop when that
+  // step is the workgroup's last; at step 0 the held weights are zero and
+  // the values read are step 0's.
+  uint4 pb[NB] = {};
+  const int compute_steps =
+      kDeferPV ? (wave_steps > 0 ? min(wave_steps + 1, nsteps) : 0) : wave_steps;
   auto step = [&](int st, Scores& cur, Scores& next) {
     if constexpr (kTileInBlock) {
       rows_landed();
@@ -501,14 +532,16 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       if (st + 2 < nsteps) load_step(st + 2, R);
     }
     __syncthreads();
-    const bool computes = st < wave_steps;
+    const bool computes = st < compute_steps;
     Keys kr;
     uint4 avs[PC::NT];
     if (computes) {
-      // the next step's keys (past the last step: whatever the stage holds,
-      // unused), this step's values
+      // the values of this step (of the step before, deferred: read first,
+      // as the first products use them), the next step's keys (past the last
+      // step: whatever the stage holds, unused)
+      const int vs = kDeferPV ? (st > 0 ? st - 1 : 0) : st;
+      read_v32<DT, D, PC::NT>(avs, lds_v + __builtin_amdgcn_readfirstlane(stage_of(vs)));
       read_k(st + 1, kr);
-      read_v32<DT, D, PC::NT>(avs, lds_v + __builtin_amdgcn_readfirstlane(stage_of(st)));
     }
     if constexpr (kTileInBlock) {
       if (st + 2 < nsteps) {
@@ -528,10 +561,18 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       live[b][0] = min(kTileTokens, max(0, before));
       live[b][1] = min(kTileTokens, max(0, before - kTileTokens));
     }
-    prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
-    qk(kr, next);
-    prefill_weights<DT, D, NB>(cols, scale, cur);
-    accumulate32<DT, D, NB, PC::NT>(cols, avs);
+    if constexpr (kDeferPV) {
+      accumulate_packed<DT, D, NB, PC::NT>(cols, avs, pb);
+      prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
+      qk(kr, next);
+      prefill_weights<DT, D, NB>(cols, scale, cur);
+      pack_weights<DT, D, NB>(cols, pb);
+    } else {
+      prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
+      qk(kr, next);
+      prefill_weights<DT, D, NB>(cols, scale, cur);
+      accumulate32<DT, D, NB, PC::NT>(cols, avs);
+    }
   };
 
   if constexpr (kTileInBlock) {
@@ -555,6 +596,14 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     step(st, SA, SB);
     if (st + 1 >= nsteps) break;
     step(st + 1, SB, SA);
+  }
+  if constexpr (kDeferPV) {
+    // the last step's products, when that step is the workgroup's last
+    if (wave_steps > 0 && wave_steps == nsteps) {
+      uint4 avs[PC::NT];
+      read_v32<DT, D, PC::NT>(avs, lds_v + __builtin_amdgcn_readfirstlane(stage_of(nsteps - 1)));
+      accumulate_packed<DT, D, NB, PC::NT>(cols, avs, pb);
+    }
   }
 
 #pragma unroll
