@@ -30,7 +30,8 @@ namespace {
 // column blocks read them: keys as the A operand of S^T = K . Q^T (row-wise
 // reads), values through transposed reads for O^T += V^T . P^T (rows padded:
 // PrefillLds).  When tiles lie inside blocks the rows go from memory straight
-// into LDS (LDS-direct buffer loads, one row per instruction), and a step's
+// into LDS (LDS-direct buffer loads: key rows packed, four or eight per
+// instruction; value rows one per instruction), and a step's
 // P.V products are issued at the start of the next step, ahead of that step's
 // softmax reference, so that each wave's matrix and vector work overlap; the
 // values are then read a step later, so four LDS stages rotate.  Smaller
@@ -228,15 +229,36 @@ __device__ __forceinline__ void prefill_weights(PrefillCols<DT, D> (&cols)[NB], 
 // and every read address is a per-lane base plus a constant.  The staging
 // writes take rows r, r + 8 (r, r + 4, r + 8, r + 12 for 128-byte rows) in
 // one pass, whose 256-byte spans are disjoint modulo 512 bytes.
-template <int DT, int D>
+//
+// Packed keys (rows straight from memory): key rows unpadded, the 16-byte
+// chunks of row r permuted, chunk ch stored at ch ^ key_swizzle(r).  Then the
+// 16 rows of a key read start on two bank offsets, and the permutation sends
+// the two chunks each of their lanes reads to 32 distinct groups of 4 banks.
+// A 16-byte LDS-direct load fills four (eight) whole rows: each lane fetches
+// the memory chunk its LDS place holds.
+template <int DT, int D, bool kPackedKeys = false>
 struct PrefillLds {
   static constexpr int kRowBytes = Geo<DT, D, 16>::kRowBytes;
-  static constexpr int kKeyStride = kRowBytes + 32;
+  static constexpr int kKeyStride = kPackedKeys ? kRowBytes : kRowBytes + 32;
   static constexpr int kValStride = kRowBytes + 32;
   static constexpr int kStepRows = 2 * kTileTokens;
   static constexpr int kValOffset = kStepRows * kKeyStride;
   static constexpr int kStageBytes = kValOffset + kStepRows * kValStride;
+  static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks of a row
+  static constexpr int kBankRows = 512 / kRowBytes;     // rows per 128 four-byte banks
 };
+// A 16-byte-per-lane LDS-direct load (gfx950): lane l's 16 bytes at dst + 16 l.
+// (A device function of its own: the host compilation pass, which checks the
+// builtin's size against no gfx950 target, never sees the call.)
+__device__ __forceinline__ void lds_direct_load16(__amdgpu_buffer_rsrc_t r, lds_char* dst,
+                                                  int voffset) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, 0, 0, 0);
+}
+template <int DT, int D>
+__device__ __forceinline__ int key_swizzle(int r) {
+  using LS = PrefillLds<DT, D, true>;
+  return 2 * ((r / LS::kBankRows) % (LS::kChunks / 2));
+}
 
 // O^T += V^T . P^T over a 32-key step for every column block, in two parts:
 // read_v32 reads the A operand chunks, accumulate32 does the products.  The
@@ -304,7 +326,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   constexpr int kStepRows = 2 * kTileTokens;              // keys per step
   constexpr int kLoadRows = kThreads / CPR;               // rows per load instruction
   constexpr int kLoads = kStepRows / kLoadRows;           // per matrix and step
-  using LS = PrefillLds<DT, D>;
+  using LS = PrefillLds<DT, D, kTileInBlock>;
   constexpr int kStageBytes = LS::kStageBytes;            // keys, then values
   // Tiles inside blocks: a step's P.V waits for the next step (deferred), so
   // a stage is read until the step after its own and four stages rotate.
@@ -425,15 +447,28 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     return blk * blk_rows + head_rows + (t & bmask);
   };
   // tiles inside blocks: the rows of step st go from memory straight into
-  // LDS stage st % kStages, one 4-byte-per-lane load per row (the row lands
-  // at its padded place; rows past T, and a tile past the last position,
+  // LDS stage st % kStages (rows past T, and a tile past the last position,
   // read as zeros).  Wave w moves step rows 8w .. 8w + 7 of the keys and of
-  // the values, which lie in one tile.
+  // the values, which lie in one tile: the keys 16 bytes a lane, whole rows
+  // per load in their packed, permuted place; the values 4 bytes a lane, one
+  // row per load at its padded place.
   constexpr int kRowsPerWave = kStepRows / kPrefillWaves;
   constexpr int kRowLanes = kRowBytes / 4;
+  constexpr int kKeyRowsPerLoad = kWave / LS::kChunks;
+  constexpr int kKeyLoads = kRowsPerWave / kKeyRowsPerLoad;
   static_assert(kRowsPerWave * kPrefillWaves == kStepRows && kTileTokens % kRowsPerWave == 0 &&
-                    kRowLanes <= kWave,
+                    kRowLanes <= kWave && kRowsPerWave % kKeyRowsPerLoad == 0,
                 "direct row loads");
+  // this lane's memory offset, within its tile, for each packed key load:
+  // row r0 + i * kKeyRowsPerLoad + lane / kChunks, the chunk whose place is
+  // chunk lane % kChunks of that row
+  int key_off[kKeyLoads];
+#pragma unroll
+  for (int i = 0; i < kKeyLoads; ++i) {
+    const int sr = wave * kRowsPerWave + i * kKeyRowsPerLoad + lane / LS::kChunks;
+    const int ch = (lane % LS::kChunks) ^ key_swizzle<DT, D>(sr);
+    key_off[i] = (sr % kTileTokens) * kRowBytes + 16 * ch;
+  }
   // byte offset of step st's LDS stage, unsigned so that the compiler can
   // fold each read's constant part into the instruction's offset field
   auto stage_of = [](int st) -> uint32_t { return uint32_t(st) % kStages * kStageBytes; };
@@ -442,12 +477,14 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     const int k = 2 * st + r0 / kTileTokens;
     const __amdgpu_buffer_rsrc_t rk = rsrc(kbase, k), rv = rsrc(vbase, k);
     lds_char* const sb = (lds_char*)lds + stage_of(st);
+#pragma unroll
+    for (int i = 0; i < kKeyLoads; ++i)
+      lds_direct_load16(rk, sb + (r0 + i * kKeyRowsPerLoad) * LS::kKeyStride, key_off[i]);
     if (lane < kRowLanes) {
 #pragma unroll
       for (int i = 0; i < kRowsPerWave; ++i) {
         const int sr = r0 + i;
         const int off = (sr % kTileTokens) * kRowBytes + 4 * lane;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, sb + sr * LS::kKeyStride, 4, off, 0, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, sb + LS::kValOffset + sr * LS::kValStride, 4,
                                                  off, 0, 0, 0);
       }
@@ -490,14 +527,21 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   // the products
   using Scores = f32x4[NB][2];
   using Keys = KeyRegs<DT, D>[2];
+  // lane (gq, c) reads key row c of each half, chunks 4kk + gq (packed keys:
+  // at their permuted places, the same in both halves)
+  int key_rd[KK];
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+    key_rd[kk] = c * LS::kKeyStride +
+                 16 * (kTileInBlock ? (4 * kk + gq) ^ key_swizzle<DT, D>(c) : 4 * kk + gq);
   auto read_k = [&](int st, Keys& kr) {
-    const char* kb = lds + stage_of(st) + c * LS::kKeyStride + gq * 16;
+    const char* kb = lds + __builtin_amdgcn_readfirstlane(stage_of(st));
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk)
-        kr[h].k[kk] = *reinterpret_cast<const uint4*>(kb + h * kTileTokens * LS::kKeyStride +
-                                                      64 * kk);
+        kr[h].k[kk] =
+            *reinterpret_cast<const uint4*>(kb + key_rd[kk] + h * kTileTokens * LS::kKeyStride);
   };
   auto qk = [&](const Keys& kr, Scores& sc) {
 #pragma unroll
