@@ -231,11 +231,11 @@ __device__ __forceinline__ void prefill_weights(PrefillCols<DT, D> (&cols)[NB], 
 // one pass, whose 256-byte spans are disjoint modulo 512 bytes.
 //
 // Packed keys (rows straight from memory): key rows unpadded, the 16-byte
-// chunks of row r permuted, chunk ch stored at ch ^ key_swizzle(r).  Then the
-// 16 rows of a key read start on two bank offsets, and the permutation sends
-// the two chunks each of their lanes reads to 32 distinct groups of 4 banks.
-// A 16-byte LDS-direct load fills four (eight) whole rows: each lane fetches
-// the memory chunk its LDS place holds.
+// chunks of row r rotated, chunk ch stored at (ch + 2r) mod kChunks: the same
+// 32-byte shift per row that the padding gives, inside the row.  The bank
+// counter reads no conflict for it (XOR permutations of the chunks left
+// conflicts).  A 16-byte LDS-direct load fills four (eight) whole rows: each
+// lane fetches the memory chunk its LDS place holds.
 template <int DT, int D, bool kPackedKeys = false>
 struct PrefillLds {
   static constexpr int kRowBytes = Geo<DT, D, 16>::kRowBytes;
@@ -245,7 +245,6 @@ struct PrefillLds {
   static constexpr int kValOffset = kStepRows * kKeyStride;
   static constexpr int kStageBytes = kValOffset + kStepRows * kValStride;
   static constexpr int kChunks = kRowBytes / 16;        // 16-byte chunks of a row
-  static constexpr int kBankRows = 512 / kRowBytes;     // rows per 128 four-byte banks
 };
 // A 16-byte-per-lane LDS-direct load (gfx950): lane l's 16 bytes at dst + 16 l.
 // (A device function of its own: the host compilation pass, which checks the
@@ -254,10 +253,15 @@ __device__ __forceinline__ void lds_direct_load16(__amdgpu_buffer_rsrc_t r, lds_
                                                   int voffset) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, dst, 16, voffset, 0, 0, 0);
 }
+// The packed-key place of memory chunk ch of step row r, and the memory
+// chunk at place p.
 template <int DT, int D>
-__device__ __forceinline__ int key_swizzle(int r) {
-  using LS = PrefillLds<DT, D, true>;
-  return 2 * ((r / LS::kBankRows) % (LS::kChunks / 2));
+__device__ __forceinline__ int key_place(int r, int ch) {
+  return (ch + 2 * r) & (PrefillLds<DT, D, true>::kChunks - 1);
+}
+template <int DT, int D>
+__device__ __forceinline__ int key_chunk_at(int r, int p) {
+  return (p - 2 * r) & (PrefillLds<DT, D, true>::kChunks - 1);
 }
 
 // O^T += V^T . P^T over a 32-key step for every column block, in two parts:
@@ -450,7 +454,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   // LDS stage st % kStages (rows past T, and a tile past the last position,
   // read as zeros).  Wave w moves step rows 8w .. 8w + 7 of the keys and of
   // the values, which lie in one tile: the keys 16 bytes a lane, whole rows
-  // per load in their packed, permuted place; the values 4 bytes a lane, one
+  // per load in their packed, rotated place; the values 4 bytes a lane, one
   // row per load at its padded place.
   constexpr int kRowsPerWave = kStepRows / kPrefillWaves;
   constexpr int kRowLanes = kRowBytes / 4;
@@ -466,7 +470,7 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
 #pragma unroll
   for (int i = 0; i < kKeyLoads; ++i) {
     const int sr = wave * kRowsPerWave + i * kKeyRowsPerLoad + lane / LS::kChunks;
-    const int ch = (lane % LS::kChunks) ^ key_swizzle<DT, D>(sr);
+    const int ch = key_chunk_at<DT, D>(sr, lane % LS::kChunks);
     key_off[i] = (sr % kTileTokens) * kRowBytes + 16 * ch;
   }
   // byte offset of step st's LDS stage, unsigned so that the compiler can
@@ -528,12 +532,13 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
   using Scores = f32x4[NB][2];
   using Keys = KeyRegs<DT, D>[2];
   // lane (gq, c) reads key row c of each half, chunks 4kk + gq (packed keys:
-  // at their permuted places, the same in both halves)
+  // at their rotated places, the same in both halves: 2 (c + 16) = 2c modulo
+  // the chunks of a row)
   int key_rd[KK];
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
     key_rd[kk] = c * LS::kKeyStride +
-                 16 * (kTileInBlock ? (4 * kk + gq) ^ key_swizzle<DT, D>(c) : 4 * kk + gq);
+                 16 * (kTileInBlock ? key_place<DT, D>(c, 4 * kk + gq) : 4 * kk + gq);
   auto read_k = [&](int st, Keys& kr) {
     const char* kb = lds + __builtin_amdgcn_readfirstlane(stage_of(st));
 #pragma unroll
