@@ -152,38 +152,59 @@ __device__ __forceinline__ void prefill_qk32(const PrefillCols<DT, D>& t,
 // A step's softmax for every column block from its raw scores (S^T = K . Q^T
 // per half, lane (gq, c) holding keys 4gq .. 4gq+3 of each half; the query
 // rows carry the sign of the scale, so `scale` is its magnitude in log2
-// units), in two parts.  The reference: mask on diagonal steps (in place),
-// then one wave-uniform test whether any lane's raw maximum exceeds its
+// units), in two parts.  The reference: each lane's raw maxima (on diagonal
+// steps taken again after masking, in place), then one wave-uniform test
+// whether any lane's raw maximum exceeds its
 // column's bound `lim` (the reference plus kRefSlack, in raw units); only then
 // are the column maxima formed and the reference moved, with the rescale.
 // The weights: exp2(raw * scale - m) with the scale inside the FMA.  Between
 // the two the next step's score products are issued, so that they run on the
 // matrix cores while the weights are computed.
-template <int DT, int D, int NB>
+template <int DT, int D, int NB, bool kAfterProducts>
 __device__ __forceinline__ void prefill_reference(PrefillCols<DT, D> (&cols)[NB], float scale,
                                                   f32x4 (&sc)[NB][2], int gq, bool mask,
                                                   const int (&live)[NB][2]) {
-  float mx[NB];
-  bool move = false;
+  auto maxima = [&](float (&mx)[NB]) {
 #pragma unroll
-  for (int b = 0; b < NB; ++b) {
-    // keys after a column's position (a wave-uniform branch: steps on the
-    // diagonal only)
-    if (mask) {
+    for (int b = 0; b < NB; ++b) {
+      float m = sc[b][0][0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][0][i]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][1][i]);
+      mx[b] = m;
+    }
+  };
+  // The raw maxima come first, ahead of the masking branch, so that they
+  // share one scheduling region with the products issued just before (the
+  // deferred P.V: kAfterProducts).  There the order is set: eight products
+  // back to back (by then the scores of the step before have left the
+  // matrix cores), then one product per two vector instructions, then the
+  // rest.  Steps on the diagonal mask and take the maxima again.
+  float mx[NB];
+  maxima(mx);
+  if constexpr (kAfterProducts) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // matrix products
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 2, 0); // vector instructions
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+  }
+  if (mask) {
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         if (4 * gq + i >= live[b][0]) sc[b][0][i] = -INFINITY;
         if (4 * gq + i >= live[b][1]) sc[b][1][i] = -INFINITY;
       }
-    }
-    float m = sc[b][0][0];
-#pragma unroll
-    for (int i = 1; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][0][i]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = __builtin_elementwise_maximum(m, sc[b][1][i]);
-    mx[b] = m;
-    move |= m > cols[b].lim;
+    maxima(mx);
   }
+  bool move = false;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) move |= mx[b] > cols[b].lim;
   if (__builtin_amdgcn_ballot_w64(move) != 0) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
@@ -612,12 +633,12 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
     }
     if constexpr (kDeferPV) {
       accumulate_packed<DT, D, NB, PC::NT>(cols, avs, pb);
-      prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
+      prefill_reference<DT, D, NB, true>(cols, scale, cur, gq, mask, live);
       qk(kr, next);
       prefill_weights<DT, D, NB>(cols, scale, cur);
       pack_weights<DT, D, NB>(cols, pb);
     } else {
-      prefill_reference<DT, D, NB>(cols, scale, cur, gq, mask, live);
+      prefill_reference<DT, D, NB, false>(cols, scale, cur, gq, mask, live);
       qk(kr, next);
       prefill_weights<DT, D, NB>(cols, scale, cur);
       accumulate32<DT, D, NB, PC::NT>(cols, avs);
