@@ -637,6 +637,14 @@ __global__ __launch_bounds__(kWave * kPrefillWaves, 2) void prefill_kernel(Decod
       qk(kr, next);
       prefill_weights<DT, D, NB>(cols, scale, cur);
       pack_weights<DT, D, NB>(cols, pb);
+      // the next step's score products spread evenly through the weights:
+      // one product per two vector instructions (the compiler's own order
+      // left most products at the end, after the exponentials)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // matrix product
+        __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);   // vector instructions
+      }
     } else {
       prefill_reference<DT, D, NB, false>(cols, scale, cur, gq, mask, live);
       qk(kr, next);
